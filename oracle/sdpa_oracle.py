@@ -1,0 +1,226 @@
+"""CPU oracle for scaled dot-product attention, forward and backward, in float64.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module; only the tests, the package smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP library: it is the
+plain definition written out with numpy, slow and obviously correct.
+
+Sources, by page (the pages are the authority on what is computed):
+
+* The JAX attention codelab ("Speed up attention on GPU with cuDNN and
+  TransformerEngine"), step 1 "how attention works": the formula
+  softmax(Q K^T / sqrt(d_k)) V and its four steps (scores, scale + softmax,
+  weights times V, output of Q's shape). Step 4 "attention from scratch":
+  the dense, materialised form this module follows.
+* Same codelab, step 7 "add a causal mask": each position attends only to
+  itself and earlier positions (lower-triangular mask).
+* Same codelab, step 9 "MHA, GQA, MQA": K/V carry fewer heads; each KV head is
+  shared by a contiguous group of query heads (read: kv = hq // (h_q / h_kv)).
+* The cuDNN 9 blog ("Accelerating Transformers with NVIDIA cuDNN 9"),
+  "SDPA as a cuDNN graph" (Figure 4) and the C++ block of "SDPA usage":
+  attn_scale multiplies the first matmul's output before the mask and softmax;
+  the SDPA node also returns ``stats`` for training.
+* Same codelab, step 10 "FP8 path": E4M3 (4 exponent bits, 3 mantissa bits)
+  in the forward pass.
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+
+* ``stats`` is the natural-log logsumexp of the scaled, masked scores of each
+  query row: LSE_i = m_i + ln(sum_j exp(S_ij - m_i)), m_i = max_j S_ij.
+* the causal mask is top-left aligned: key j is visible to query i iff j <= i,
+  also when s_q != s_kv.
+* the backward is the exact gradient of the forward (the pages only show that
+  a forward+backward exists), with D_i = sum_d dO_id * O_id.
+* fp8 inputs are the e4m3 codes times a per-tensor fp32 descale; the oracle
+  does not quantise P (exact softmax), so the fp8 kernel's P rounding is what
+  the fp8 tolerance absorbs.
+
+Memory: rows of queries are processed in blocks so that a (block x s_kv)
+score matrix, not (s_q x s_kv), is live. Each row's softmax still spans all of
+its keys; for the backward, dK and dV are summed over query blocks (the same
+sum, re-associated) — no other reordering.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_ROW_BLOCK = 512
+
+
+def _kv_head(hq: int, h_q: int, h_kv: int) -> int:
+    """KV head read by query head hq: contiguous groups of h_q / h_kv query heads."""
+    if h_q % h_kv != 0:
+        raise ValueError("h_q must be a multiple of h_kv")
+    return hq // (h_q // h_kv)
+
+
+def _masked_scores(q_rows: np.ndarray, row_idx: np.ndarray, kh: np.ndarray,
+                   scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T for the given query rows, with masked entries set to -inf."""
+    s = scale * (q_rows @ kh.T)
+    if causal:
+        key_idx = np.arange(kh.shape[0])
+        s = np.where(key_idx[None, :] <= row_idx[:, None], s, -np.inf)
+    return s
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row softmax of S: returns (P, m, l) with P = exp(S - m) / l."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, m[:, 0], l[:, 0]
+
+
+def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                      causal: bool, heads=None, rows=None, row_block: int = _ROW_BLOCK):
+    """Forward pass O = softmax(scale * Q K^T + mask) V and LSE, in float64.
+
+    Follows the JAX attention codelab's step 1 formula and step 4 dense form
+    (scores, scale, row softmax, weights times V), with step 7's causal mask,
+    step 9's KV-head groups and the ``stats`` output of the cuDNN 9 blog's
+    SDPA node (read as the natural-log logsumexp of each row).
+
+    q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d), any real dtype (cast to float64).
+    heads: optional list of (b, hq) pairs to compute (default: all).
+    rows: optional array of query-row indices to compute (default: all).
+    Returns (O, LSE): O has shape (b, h_q, n_rows, d) and LSE (b, h_q, n_rows);
+    entries for heads not in ``heads`` are NaN.
+    """
+    b, h_q, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    row_idx_all = np.arange(s_q) if rows is None else np.asarray(rows)
+    n = row_idx_all.shape[0]
+    out = np.full((b, h_q, n, d), np.nan)
+    lse = np.full((b, h_q, n), np.nan)
+    pairs = [(bi, hi) for bi in range(b) for hi in range(h_q)] if heads is None else heads
+    for bi, hq in pairs:
+        g = _kv_head(hq, h_q, h_kv)
+        kh = np.asarray(k[bi, g], dtype=np.float64)
+        vh = np.asarray(v[bi, g], dtype=np.float64)
+        for r0 in range(0, n, row_block):
+            ridx = row_idx_all[r0:r0 + row_block]
+            qr = np.asarray(q[bi, hq][ridx], dtype=np.float64)
+            s = _masked_scores(qr, ridx, kh, scale, causal)
+            p, m, l = _softmax_rows(s)
+            out[bi, hq, r0:r0 + len(ridx)] = p @ vh
+            lse[bi, hq, r0:r0 + len(ridx)] = m + np.log(l)
+    return out, lse
+
+
+def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+    """The full attention-weight tensor P (b, h_q, s_q, s_kv); small inputs only.
+
+    The "weights" of the JAX attention codelab's step 1 (rows sum to one).
+    """
+    b, h_q, s_q, _ = q.shape
+    h_kv = k.shape[1]
+    p_all = np.zeros((b, h_q, s_q, k.shape[2]))
+    for bi in range(b):
+        for hq in range(h_q):
+            kh = np.asarray(k[bi, _kv_head(hq, h_q, h_kv)], dtype=np.float64)
+            s = _masked_scores(np.asarray(q[bi, hq], dtype=np.float64), np.arange(s_q), kh,
+                               scale, causal)
+            p_all[bi, hq] = _softmax_rows(s)[0]
+    return p_all
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                       scale: float, causal: bool, kv_heads=None, row_block: int = _ROW_BLOCK):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO) for the forward above, in float64.
+
+    The pages show only that a forward+backward SDPA exists (the cuDNN 9 blog,
+    Figure 2); this is the exact gradient of ``attention_forward``, derived by
+    the chain rule through the row softmax.
+
+    For each query head hq (KV head g = hq // G), with P the softmax of the
+    scaled, masked scores and O = P V:
+        D_i  = sum_d dO_id O_id
+        dV_g += P^T dO
+        dP   = dO V_g^T
+        dS   = P * (dP - D[:, None])
+        dQ   = scale * dS K_g
+        dK_g += scale * dS^T Q
+    dK and dV of a KV head are summed over every query head of its group.
+    kv_heads: optional list of (b, g) pairs to compute (default: all); the
+    other entries are NaN. dQ is filled for the query heads of those groups.
+    """
+    b, h_q, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    grp = h_q // h_kv
+    dq = np.full((b, h_q, s_q, d), np.nan)
+    dk = np.full((b, h_kv, s_kv, d), np.nan)
+    dv = np.full((b, h_kv, s_kv, d), np.nan)
+    groups = [(bi, g) for bi in range(b) for g in range(h_kv)] if kv_heads is None else kv_heads
+    for bi, g in groups:
+        kh = np.asarray(k[bi, g], dtype=np.float64)
+        vh = np.asarray(v[bi, g], dtype=np.float64)
+        dk_g = np.zeros((s_kv, d))
+        dv_g = np.zeros((s_kv, d))
+        for hq in range(g * grp, (g + 1) * grp):
+            assert _kv_head(hq, h_q, h_kv) == g
+            qh = np.asarray(q[bi, hq], dtype=np.float64)
+            doh = np.asarray(dout[bi, hq], dtype=np.float64)
+            dq_h = np.zeros((s_q, d))
+            for r0 in range(0, s_q, row_block):
+                ridx = np.arange(r0, min(s_q, r0 + row_block))
+                qr, dor = qh[ridx], doh[ridx]
+                p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal))
+                o = p @ vh
+                dvec = (dor * o).sum(axis=1)
+                dv_g += p.T @ dor
+                dp = dor @ vh.T
+                ds = p * (dp - dvec[:, None])
+                dq_h[ridx] = scale * (ds @ kh)
+                dk_g += scale * (ds.T @ qr)
+            dq[bi, hq] = dq_h
+        dk[bi, g] = dk_g
+        dv[bi, g] = dv_g
+    return dq, dk, dv
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP e4m3fn codes (uint8) as float64.
+
+    The JAX attention codelab, step 10, names E4M3 (4 exponent bits, 3
+    mantissa bits) for the forward pass; the bit layout is the OCP e4m3fn one.
+
+    Layout s eeee mmm, exponent bias 7. e = 0: subnormal (m / 8) * 2^-6.
+    e = 15 and m = 7: NaN (the format has no infinities); every other code is
+    (1 + m / 8) * 2^(e - 7). Largest finite value 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = (1.0 + m / 8.0) * np.power(2.0, e - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def fp8_dequantize(codes: np.ndarray, descale: float) -> np.ndarray:
+    """Real values x = e4m3(code) * descale that an fp8 kernel receives."""
+    return fp8_e4m3_decode(codes) * float(descale)
+
+
+def sdpa_flops(b: int, h_q: int, s_q: int, s_kv: int, d: int, causal: bool) -> float:
+    """Counted forward flops 4*b*h*s_q*s_kv*d, halved under the causal mask."""
+    f = 4.0 * b * h_q * s_q * s_kv * d
+    return f / 2 if causal else f
+
+
+__all__ = [
+    "attention_forward", "attention_backward", "attention_probs",
+    "fp8_e4m3_decode", "fp8_dequantize", "sdpa_flops",
+]
+
+if __name__ == "__main__":  # pragma: no cover - tiny self-demo
+    rng = np.random.default_rng(0)
+    qq, kk, vv = (rng.standard_normal((1, 2, 4, 3)) for _ in range(3))
+    o, l = attention_forward(qq, kk, vv, 1 / math.sqrt(3), True)
+    print(o[0, 0], l[0, 0])
