@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = one forward (O, LSE) and one backward (dQ, dK, dV) of causal
+scaled dot-product attention with head dim 128 in bf16, on the s=8192 point of
+the head-dim-128 sweep (b=2, h=16, b*s = 16384 tokens, BSHD layout), all
+inputs resident in HBM. The reported value is TFLOP/s of the whole step under
+the counting 4*b*h*s_q*s_kv*d per forward (halved under the causal mask) and
+2.5x that per backward, as in the cuDNN 9 blog's forward and forward+backward
+figures (Figures 1 and 2). GPU time only (events on the launch stream), the
+convention the blog states for its measurements.
+
+Prints one JSON line on stdout. Also reports:
+  * roofline: the dominant kernel's achieved TFLOP/s (its own matmul flops per
+    launch / its mean duration from events recorded around it inside the
+    library) against the MI355X dense bf16 MFMA peak;
+  * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
+    workload (a few (b, h) heads, forward + backward) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls needed to time kernels with events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+
+def cpu_baseline(w, ins, n_heads: int) -> dict:
+    """Time the float64 oracle (as it stands) on n_heads (b, h) heads, fwd + bwd."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_backward, attention_forward
+
+    heads = [(0, h) for h in range(n_heads)]
+    # only the sampled heads are converted to float64
+    q = np.stack([ins["q"][0, h].double().numpy() for _, h in heads])[None]
+    k = np.stack([ins["k"][0, h].double().numpy() for _, h in heads])[None]
+    v = np.stack([ins["v"][0, h].double().numpy() for _, h in heads])[None]
+    do = np.stack([ins["do"][0, h].double().numpy() for _, h in heads])[None]
+    t0 = time.perf_counter()
+    attention_forward(q, k, v, w.scale, w.causal)
+    attention_backward(q, k, v, do, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4.0 * n_heads * w.s_q * w.s_kv * w.d / (2 if w.causal else 1)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_heads} of {w.b * w.h_q} (b, h) heads of the same workload, forward + backward, "
+                      f"float64 numpy; {dt:.2f} s wall",
+            "seconds": round(dt, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path.", file=sys.stderr)
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py is single-process, single-GPU", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import scaled_dot_product_04_amd as sdpa
+    import sdpa_inputs
+
+    w = sdpa_inputs.hd128(args.seq)
+    log(f"[bench] workload {w.name}: b={w.b} h={w.h_q} s={w.s_q} d={w.d} bf16 causal BSHD")
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    dev = torch.device("cuda:0")
+    g = {k: sdpa_inputs.to_device_like(v, dev) for k, v in ins.items() if isinstance(v, torch.Tensor)}
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    ws = torch.empty(max(16, sdpa.bwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, w.causal,
+                                                     torch.bfloat16)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    lib = sdpa.load_library()
+    lib.sdpa_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    hip = Hip()
+
+    def step(ev=None):
+        if ev is not None:
+            lib.sdpa_set_timing_events((ctypes.c_void_p * 2)(*ev[0:2]), 2)
+        sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, stream=stream)
+        if ev is not None:
+            lib.sdpa_set_timing_events((ctypes.c_void_p * 4)(*ev[2:6]), 4)
+        sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv,
+                 workspace=ws, stream=stream)
+        if ev is not None:
+            lib.sdpa_set_timing_events(None, 0)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[hip.event().value for _ in range(6)] for _ in range(args.steps)]
+    start, stop = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(start, sh)
+    for i in range(args.steps):
+        step(events[i])
+    hip.record(stop, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.ms(start, stop)
+    ms_step = total_ms / args.steps
+
+    per = {"fwd": [], "bwd_delta": [], "bwd_dkdv": [], "bwd_dq": []}
+    for ev in events:
+        per["fwd"].append(hip.ms(ev[0], ev[1]))
+        per["bwd_delta"].append(hip.ms(ev[2], ev[3]))
+        per["bwd_dkdv"].append(hip.ms(ev[3], ev[4]))
+        per["bwd_dq"].append(hip.ms(ev[4], ev[5]))
+    mean = {k: statistics.fmean(v) for k, v in per.items()}
+    med = {k: statistics.median(v) for k, v in per.items()}
+
+    F = w.fwd_flops                      # counted forward flops
+    step_flops = 3.5 * F                 # forward + backward (2.5x)
+    value = step_flops / (ms_step / 1e3) / 1e12
+    fwd_tflops = F / (med["fwd"] / 1e3) / 1e12
+    bwd_ms = med["bwd_delta"] + med["bwd_dkdv"] + med["bwd_dq"]
+    bwd_tflops = 2.5 * F / (bwd_ms / 1e3) / 1e12
+    # matmul flops each kernel performs per launch (per (b, h) head: s_q*s_kv*d*2 per matmul, halved causal)
+    mm = F / 2.0
+    kernel_flops = {"fwd": 2 * mm, "bwd_dkdv": 4 * mm, "bwd_dq": 3 * mm}
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda k: mean[k])
+    achieved = kernel_flops[dom] / (mean[dom] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms_mean": round(mean[dom], 4)}
+    log(f"[bench] per-kernel median ms: " + ", ".join(f"{k}={v:.3f}" for k, v in med.items()))
+    log(f"[bench] fwd {fwd_tflops:.1f} TFLOP/s ({100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% peak); "
+        f"bwd {bwd_tflops:.1f}; fwd+bwd {value:.1f} ({100 * value / PEAK_BF16_TFLOPS:.1f}%)")
+
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline(w, ins, args.cpu_heads)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    out = {
+        "metric": "SDPA fwd and fwd+bwd TFLOPS and % of MFMA peak, hd128 causal bf16",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "b": w.b, "h_q": w.h_q, "h_kv": w.h_kv, "s_q": w.s_q, "s_kv": w.s_kv,
+                   "d": w.d, "causal": True, "layout": "bshd", "step": "forward + backward",
+                   "parallelism": "single GPU"},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_bwd_tflops": round(value, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

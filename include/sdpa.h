@@ -1,0 +1,168 @@
+/*
+ * sdpa.h — fused scaled dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every batch b and query head hq (KV head g = hq / (h_q / h_kv)):
+ *
+ *     S   = attn_scale * Q K^T                  (first matmul, then the scale)
+ *     S_ij = -inf where causal and j > i         (top-left aligned causal mask)
+ *     O   = softmax_rows(S) V
+ *     LSE_i = ln sum_j exp(S_ij)                (the per-row softmax statistics)
+ *
+ * and its exact gradient (dQ, dK, dV) given dO. dK/dV of a KV head are summed
+ * over the query heads that share it (GQA / MQA).
+ *
+ * Sources: the formula and its four steps are those of the JAX attention
+ * codelab ("Speed up attention on GPU with cuDNN and TransformerEngine"),
+ * step 1; the causal mask its step 7; KV-head sharing its step 9; FP8 E4M3
+ * inputs its step 10. The scale applied to the first matmul's output, the
+ * causal-mask lowering and the ``stats`` output come from the cuDNN 9 blog
+ * ("Accelerating Transformers with NVIDIA cuDNN 9"), "SDPA as a cuDNN graph"
+ * (Figure 4) and "SDPA usage". The strided logical (b, h, s, d) tensors with a
+ * BSHD physical layout, the io/compute dtype split and the
+ * execute(pointers, workspace) flow come from "Using cuDNN in Python".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a caller-owned DEVICE pointer. The library never
+ *    allocates, frees or retains caller memory.
+ *  - Tensors are logical (b, h, s, d). Each has a 4-entry stride array, in
+ *    ELEMENTS, in that logical order; the d stride must be 1. BSHD is
+ *    (s*h*d, d, h*d, 1), BHSD is (h*s*d, s*d, d, 1); any other strides with
+ *    a unit d stride are accepted.
+ *  - Alignment: every pointer must be 16-byte aligned and the b, h and s
+ *    strides must be multiples of 16 bytes' worth of elements; otherwise
+ *    SDPA_ERR_NOT_SUPPORTED (no silent slow path).
+ *  - Calls are asynchronous on `stream` (0 = the null stream) and return
+ *    after the kernels are enqueued; the caller synchronises.
+ *  - Validation happens before anything is enqueued. On an error nothing is
+ *    launched, the status is returned and sdpa_last_error() describes it.
+ *  - Calls are thread-safe: the only state is thread-local (the error string
+ *    and the optional timing events of sdpa_set_timing_events).
+ *  - b == 0 or s_q == 0 is an empty problem: sdpa_fwd enqueues nothing; sdpa_bwd
+ *    writes zeros to dK and dV (no query attends to them) and nothing else.
+ *  - attn_scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *  - Causal alignment is top-left: query i sees keys 0..i, also when
+ *    s_q != s_kv; every query row therefore sees at least key 0.
+ */
+#ifndef SDPA_H_
+#define SDPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDPA_F32 = 0,
+  SDPA_F16 = 1,
+  SDPA_BF16 = 2,
+  SDPA_FP8_E4M3 = 3 /* OCP e4m3fn: 4 exponent bits, 3 mantissa bits, max 448, no inf */
+} sdpa_dtype_t;
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad size, h_q % h_kv != 0, d stride != 1, ... */
+  SDPA_ERR_NOT_SUPPORTED = 2,      /* valid, but no kernel for this dtype / d / alignment */
+  SDPA_ERR_WORKSPACE_TOO_SMALL = 3,
+  SDPA_ERR_HIP = 4                 /* the HIP runtime reported an error at launch */
+} sdpa_status_t;
+
+/*
+ * Per-tensor fp8 factors (JAX attention codelab, step 10: per-tensor scaling
+ * recipe). A real input value is x = e4m3(code) * descale_x. Inside the kernel
+ * the softmax weights P (all in [0, 1]) are quantised as e4m3(P * scale_p)
+ * before the second matmul and the result is multiplied back by descale_p.
+ * The usual choice is scale_p = 448, descale_p = 1/448.
+ */
+typedef struct {
+  float descale_q;
+  float descale_k;
+  float descale_v;
+  float scale_p;
+  float descale_p;
+} sdpa_fp8_scales_t;
+
+/*
+ * Forward: O (and optionally LSE) from Q, K, V.
+ *
+ *   q       [b, h_q,  s_q,  d] in_dtype, strides q_stride
+ *   k, v    [b, h_kv, s_kv, d] in_dtype, strides k_stride / v_stride
+ *   o       [b, h_q,  s_q,  d] out_dtype, strides o_stride (written)
+ *   lse     fp32 [b][h_q][s_q], contiguous, natural log (written); NULL means
+ *           inference mode (the cuDNN node's is_inference): no statistics.
+ *   fp8     required iff in_dtype == SDPA_FP8_E4M3, else must be NULL.
+ *
+ * Supported (in_dtype -> out_dtype, d):
+ *   F32 -> F32, d in {64, 128}
+ *   F16 -> F16, BF16 -> BF16, d in {64, 128}
+ *   FP8_E4M3 -> BF16, d in {128, 256}
+ * causal in {0, 1} for all of them; any h_q multiple of h_kv.
+ */
+sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                       const int64_t q_stride[4], const int64_t k_stride[4],
+                       const int64_t v_stride[4], const int64_t o_stride[4],
+                       float attn_scale, int causal,
+                       sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
+                       const sdpa_fp8_scales_t* fp8, hipStream_t stream);
+
+/*
+ * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned
+ * use). 0 is a valid answer only for empty problems.
+ */
+size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                               int causal, sdpa_dtype_t dtype);
+
+/*
+ * Backward: dQ, dK, dV of L = sum(O * dO).
+ *
+ *   q, k, v, o, dout   as in sdpa_fwd (o is the forward's output, dout is dL/dO,
+ *                      same layout rules); dtype BF16 or F16 for all of them.
+ *   lse                the forward's LSE (fp32 [b][h_q][s_q], contiguous); required.
+ *   dq                 [b, h_q, s_q, d]  (written)
+ *   dk, dv             [b, h_kv, s_kv, d] (written; summed over each KV head's
+ *                      query-head group)
+ *   workspace          device buffer of at least sdpa_bwd_workspace_size(...)
+ *                      bytes, 16-byte aligned; its contents are scratch.
+ * Supported: BF16 and F16, d in {64, 128}, causal in {0, 1}.
+ */
+sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv,
+                       int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                       const int64_t q_stride[4], const int64_t k_stride[4],
+                       const int64_t v_stride[4], const int64_t o_stride[4],
+                       const int64_t do_stride[4], const int64_t dq_stride[4],
+                       const int64_t dk_stride[4], const int64_t dv_stride[4],
+                       float attn_scale, int causal, sdpa_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Timing hook (diagnostics only; GPU-time-only reporting as in the cuDNN 9
+ * blog's "SDPA performance" section). Registers `n` caller-created HIP events
+ * (n = 0 or events = NULL disables) that this thread's following sdpa_fwd /
+ * sdpa_bwd calls record on their stream at kernel boundaries:
+ *   sdpa_fwd: events[0] before its kernel, events[1] after it (n >= 2);
+ *   sdpa_bwd: events[0] before the D = rowsum(dO * O) kernel, events[1] after
+ *             it, events[2] after the dK/dV kernel (and its split reduction),
+ *             events[3] after the dQ kernel (n >= 4).
+ * The library does not own the events. Returns SDPA_ERR_INVALID_ARGUMENT for
+ * n < 0, n > 8, or events == NULL with n > 0.
+ */
+sdpa_status_t sdpa_set_timing_events(hipEvent_t* events, int n);
+
+/* Message describing this thread's most recent failed call ("" after a success). */
+const char* sdpa_last_error(void);
+
+/* Static name of a status code. */
+const char* sdpa_status_string(sdpa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H_ */

@@ -1,0 +1,165 @@
+"""Thin Python binding of libsdpa.so: fused scaled dot-product attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsdpa.so (declared in include/sdpa.h). torch provides device
+memory and the stream. Tensors are logical (b, h, s, d) views with any
+strides whose last (d) stride is 1 — e.g. the BSHD layout of "Using cuDNN in
+Python", (s*h*d, d, h*d, 1) — and they are passed as pointer + strides
+without copies.
+
+If libsdpa.so has not been built this module raises on first use: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_FP8_E4M3 = 0, 1, 2, 3
+STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_INVALID_ARGUMENT", 2: "SDPA_ERR_NOT_SUPPORTED",
+                3: "SDPA_ERR_WORKSPACE_TOO_SMALL", 4: "SDPA_ERR_HIP"}
+
+_DTYPE_CODES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
+                torch.float8_e4m3fn: SDPA_FP8_E4M3}
+
+_Strides = ctypes.c_int64 * 4
+
+
+class Fp8Scales(ctypes.Structure):
+    """sdpa_fp8_scales_t: per-tensor fp8 factors (x = e4m3 code value * descale)."""
+    _fields_ = [("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
+                ("descale_v", ctypes.c_float), ("scale_p", ctypes.c_float),
+                ("descale_p", ctypes.c_float)]
+
+
+class SdpaError(RuntimeError):
+    """A libsdpa call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsdpa.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int64)
+    lib.sdpa_fwd.restype = ctypes.c_int
+    lib.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, i, i,
+                             ctypes.POINTER(Fp8Scales), vp]
+    lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                             i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, i, vp,
+                             ctypes.c_size_t, vp]
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_last_error.argtypes = []
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_status_string.argtypes = [i]
+    lib.sdpa_set_timing_events.restype = ctypes.c_int
+    lib.sdpa_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().sdpa_last_error().decode()
+        raise SdpaError(status, msg)
+
+
+def _strides(t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("tensors must be logical (b, h, s, d)")
+    return _Strides(*t.stride())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _like_q(q: torch.Tensor, dtype) -> torch.Tensor:
+    """An output with q's logical shape and the same physical dim order."""
+    order = sorted(range(4), key=lambda dim: -q.stride(dim))
+    phys = torch.empty([q.shape[dim] for dim in order], dtype=dtype, device=q.device)
+    inv = [order.index(dim) for dim in range(4)]
+    return phys.permute(*inv)
+
+
+def fwd(q, k, v, *, scale: float, causal: bool, out=None, lse=None, return_lse: bool = True,
+        fp8: Fp8Scales | None = None, out_dtype=None, stream=None):
+    """O (and LSE) of fused attention. Returns (out, lse); lse is None in inference mode.
+
+    q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d); all on the GPU.
+    fp8: factors for e4m3 inputs (then out_dtype defaults to bfloat16).
+    """
+    lib = load_library()
+    b, h_q, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    in_code = _DTYPE_CODES[q.dtype]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is None:
+        out = _like_q(q, out_dtype)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
+                      _strides(q), _strides(k), _strides(v), _strides(out), float(scale), int(causal),
+                      in_code, _DTYPE_CODES[out.dtype],
+                      ctypes.byref(fp8) if fp8 is not None else None, _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, dtype) -> int:
+    return int(load_library().sdpa_bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, int(causal),
+                                                      _DTYPE_CODES[dtype]))
+
+
+def bwd(q, k, v, o, dout, lse, *, scale: float, causal: bool, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """(dQ, dK, dV) of L = sum(O * dO). dK/dV are summed over each KV head's query group."""
+    lib = load_library()
+    b, h_q, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    dq = _like_q(q, q.dtype) if dq is None else dq
+    dk = _like_q(k, k.dtype) if dk is None else dk
+    dv = _like_q(v, v.dtype) if dv is None else dv
+    if workspace is None:
+        n = bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, q.dtype)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    st = lib.sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                      _ptr(dv), b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v),
+                      _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv),
+                      float(scale), int(causal), _DTYPE_CODES[q.dtype], _ptr(workspace),
+                      workspace.numel(), _stream(stream))
+    _check(st)
+    return dq, dk, dv
+
+
+__all__ = ["fwd", "bwd", "bwd_workspace_size", "load_library", "library_path", "Fp8Scales",
+           "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3"]

@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// the 32x32x16 MFMA operand/accumulator conventions, and small LDS/global
+// access helpers.
+//
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_{bf16,f16}, wave64):
+//   A operand (32 x 16): lane l holds row i = l % 32 and 8 consecutive
+//     contraction indices selected by the lane half h = l / 32.
+//   B operand (16 x 32): lane l holds column j = l % 32 and the same 8
+//     contraction indices for its half h.
+//   Accumulator (32 x 32 fp32, 16 registers): lane l holds column j = l % 32;
+//     register r holds row 8 * (r / 4) + 4 * h + (r % 4).
+// Only the pairing "A lane (i, h, m) meets B lane (j, h, m)" matters for a
+// contraction, so any one-to-one assignment of (h, m) to contraction indices
+// works as long as both operands use the same one. When an operand is built
+// from an accumulator, its (h, m) -> index assignment is the accumulator's row
+// layout, and the operand read from LDS follows it (see key_of()).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type traits for the 16-bit MFMA paths.
+struct Bf16T {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+struct F16T {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Two fp32 values rounded to nearest-even 16-bit and packed (low = x).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef typename T::elem E;
+  E ex = (E)x, ey = (E)y;
+  uint16_t ux = __builtin_bit_cast(uint16_t, ex), uy = __builtin_bit_cast(uint16_t, ey);
+  return (uint32_t)ux | ((uint32_t)uy << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  typedef typename T::elem E;
+  return (float)__builtin_bit_cast(E, bits);
+}
+
+// Row of the 32x32 accumulator held by register r of a lane in half h.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
+
+// Contraction index (within a 16-wide k-step t) that lane half h's element m
+// stands for, when the operand is taken from accumulator registers
+// 8*(t%2) .. 8*(t%2)+7 of accumulator block t/2:  16 t + 8 (m/4) + 4 h + m%4.
+__device__ __forceinline__ constexpr int key_of(int t, int h, int m) {
+  return 16 * t + 8 * (m / 4) + 4 * h + (m % 4);
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  // max with the lane 32 apart (the other half holding the same column)
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// 4x4 transpose of 16-bit elements held as 4 rows of (lo, hi) dwords:
+// in: row r = (e[r][0] | e[r][1] << 16, e[r][2] | e[r][3] << 16)
+// out: column c = (e[0][c] | e[1][c] << 16, e[2][c] | e[3][c] << 16)
+__device__ __forceinline__ void transpose4x4_b16(const u32x2 in[4], u32x2 out[4]) {
+  out[0].x = __builtin_amdgcn_perm(in[1].x, in[0].x, 0x05040100u);
+  out[0].y = __builtin_amdgcn_perm(in[3].x, in[2].x, 0x05040100u);
+  out[1].x = __builtin_amdgcn_perm(in[1].x, in[0].x, 0x07060302u);
+  out[1].y = __builtin_amdgcn_perm(in[3].x, in[2].x, 0x07060302u);
+  out[2].x = __builtin_amdgcn_perm(in[1].y, in[0].y, 0x05040100u);
+  out[2].y = __builtin_amdgcn_perm(in[3].y, in[2].y, 0x05040100u);
+  out[3].x = __builtin_amdgcn_perm(in[1].y, in[0].y, 0x07060302u);
+  out[3].y = __builtin_amdgcn_perm(in[3].y, in[2].y, 0x07060302u);
+}
+
+}  // namespace sdpa

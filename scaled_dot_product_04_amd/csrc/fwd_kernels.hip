@@ -1,0 +1,337 @@
+// Forward kernels: fused scaled dot-product attention with online softmax.
+//
+// What is computed (JAX attention codelab, step 1 formula and step 7 causal
+// mask; cuDNN 9 blog, "SDPA as a cuDNN graph", Figure 4: the scale multiplies
+// the first matmul's output, the causal mask is an index compare + select,
+// softmax follows, then the second matmul; the node's second output "stats"
+// is the per-row logsumexp):
+//   S = scale * Q K^T, masked (j > i) under the causal flag, O = softmax(S) V,
+//   LSE_i = ln sum_j exp(S_ij).
+// The score matrix is never written to memory: each workgroup streams K/V
+// tiles through LDS and keeps a running row max m and row sum l (the flash
+// attention recurrence the cuDNN blog's "SDPA performance" section cites).
+//
+// gfx950 design (one workgroup = 4 waves = 128 query rows of one (b, head)):
+//  * each wave owns 32 query rows; it holds its Q rows in registers as the
+//    B operand of S^T = K Q^T (v_mfma_f32_32x32x16), so every lane owns one
+//    query column of S^T: the row max / row sum of the softmax are in-lane
+//    reductions plus one exchange between the two wave halves;
+//  * the exponentiated scores, packed to 16 bits, are directly the B operand
+//    of O^T += V^T P^T; V^T is read from an LDS copy of the V tile that is
+//    stored transposed (4x4 register transposes during staging);
+//  * K/V tiles of 64 keys are staged in LDS once per workgroup and shared by
+//    the 4 waves; under the causal mask, tiles entirely above the diagonal
+//    are never loaded, and diagonal tiles are masked element-wise;
+//  * workgroups are issued longest-first for the causal mask, and heads are
+//    remapped so that all query blocks of a head (and the query heads of a
+//    GQA group) run on the same XCD and share its L2.
+#include "device_common.h"
+#include "sdpa_internal.h"
+
+namespace sdpa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per K/V tile
+
+// Maps a linear workgroup id to (query block, b, head). Query blocks are
+// issued from the last (longest under the causal mask) to the first. When
+// the head count allows, consecutive heads are gathered on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin by id).
+__device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int h_q, int& qb,
+                                          int& bi, int& hq) {
+  const int rank = id / bh_total;
+  int slot = id - rank * bh_total;
+  if ((bh_total & 7) == 0) {
+    const int per = bh_total >> 3;
+    slot = (slot & 7) * per + (slot >> 3);
+  }
+  qb = n_qblk - 1 - rank;
+  bi = slot / h_q;
+  hq = slot - bi * h_q;
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
+  typedef typename T::elem E;
+  typedef typename T::vec8 V8;
+  constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
+  constexpr int VSTR = kBN + 4;  // LDS row stride (elements) of the transposed V tile
+  constexpr int NKS = D / 16;    // 16-wide contraction steps over d
+  constexpr int NDB = D / 32;    // 32-wide output blocks over d
+  constexpr int NSB = kBN / 32;  // 32-key score blocks per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  int qb, bi, hq;
+  map_block(blockIdx.x, n_qblk, a.b * a.h_q, a.h_q, qb, bi, hq);
+  const int g = hq / (a.h_q / a.h_kv);
+  const int qblk0 = qb * kBM;
+  const int q0 = qblk0 + wave * 32;
+  const int my_q = q0 + j;
+
+  const E* qp = (const E*)a.q + bi * a.qs.b + hq * a.qs.h;
+  const E* kp = (const E*)a.k + bi * a.ks.b + g * a.ks.h;
+  const E* vp = (const E*)a.v + bi * a.vs.b + g * a.vs.h;
+
+  // Q rows as the B operand of S^T = K Q^T.
+  V8 qf[NKS];
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) {
+    if (my_q < a.s_q) {
+      qf[t] = *(const V8*)(qp + (int64_t)my_q * a.qs.s + 16 * t + 8 * h);
+    } else {
+      qf[t] = V8{};
+    }
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;  // running max, in log2 units of the scaled scores
+  float l_run = 0.f;        // running sum (this lane half's keys only)
+  const float sl2 = a.scale * kLog2e;
+
+  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + kBM) : a.s_kv;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int k0 = tile * kBN;
+    __syncthreads();
+    // Stage K rows (16-byte chunks) and V (4x4 blocks, stored transposed).
+    {
+      constexpr int CH = D / 8;
+#pragma unroll
+      for (int c = tid; c < kBN * CH; c += 256) {
+        const int r = c / CH, cc = c - (c / CH) * CH;
+        u32x4 val = u32x4{0, 0, 0, 0};
+        if (k0 + r < a.s_kv) val = *(const u32x4*)(kp + (int64_t)(k0 + r) * a.ks.s + cc * 8);
+        *(u32x4*)(&Ks[r * KSTR + cc * 8]) = val;
+      }
+      constexpr int DG = D / 4;
+#pragma unroll
+      for (int c = tid; c < (kBN / 4) * DG; c += 256) {
+        const int dg = c % DG, kg = c / DG;
+        u32x2 rows[4], cols[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 4 * kg + r;
+          rows[r] = u32x2{0, 0};
+          if (key < a.s_kv) rows[r] = *(const u32x2*)(vp + (int64_t)key * a.vs.s + 4 * dg);
+        }
+        transpose4x4_b16(rows, cols);
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&Vt[(4 * dg + c2) * VSTR + 4 * kg]) = cols[c2];
+      }
+    }
+    __syncthreads();
+    if (CAUSAL && k0 > q0 + 31) continue;  // every key of this tile is above this wave's rows
+
+    // S^T = K Q^T for the 64 keys of the tile.
+    f32x16 sacc[NSB];
+#pragma unroll
+    for (int nb = 0; nb < NSB; ++nb) {
+      sacc[nb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NKS; ++t) {
+        const V8 kf = *(const V8*)(&Ks[(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
+        sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
+      }
+    }
+    // Causal / ragged-tail mask (only tiles that cross the diagonal or the end).
+    const bool need_mask = (k0 + kBN > a.s_kv) || (CAUSAL && k0 + kBN - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + nb * 32 + acc_row(r, h);
+          if (key >= a.s_kv || (CAUSAL && key > my_q)) sacc[nb][r] = -INFINITY;
+        }
+    }
+    // Online softmax: new running max, rescale of the old state.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+
+    // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand.
+    uint32_t pk[NSB][8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -m_new));
+        lsum += p0 + p1;
+        pk[nb][r / 2] = pack2<T>(p0, p1);
+      }
+    l_run += lsum;
+
+    // O^T += V^T P^T, 16 keys per step.
+#pragma unroll
+    for (int t2 = 0; t2 < kBN / 16; ++t2) {
+      const int nb = t2 / 2, base = 4 * (t2 % 2);
+      u32x4 bw = u32x4{pk[nb][base], pk[nb][base + 1], pk[nb][base + 2], pk[nb][base + 3]};
+      const V8 pb = __builtin_bit_cast(V8, bw);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* vrow = &Vt[(db * 32 + j) * VSTR + 16 * t2 + 4 * h];
+        const u32x2 lo = *(const u32x2*)(vrow);
+        const u32x2 hi = *(const u32x2*)(vrow + 8);
+        const V8 va = __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        oacc[db] = T::mfma(va, pb, oacc[db]);
+      }
+    }
+  }
+
+  // Epilogue: O = O_acc / l, LSE = ln l + m.
+  const float l_tot = wave_sum_halves(l_run);
+  const float inv = 1.f / l_tot;
+  if (my_q < a.s_q) {
+    E* op = (E*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = db * 32 + 8 * rq + 4 * h;
+        u32x2 w;
+        w.x = pack2<T>(oacc[db][4 * rq + 0] * inv, oacc[db][4 * rq + 1] * inv);
+        w.y = pack2<T>(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
+        *(u32x2*)(op + d0) = w;
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// fp32 I/O: one thread per query row, K/V tiles of 32 keys in LDS, fp32 FMA.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
+  constexpr int BN = 32;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x % (a.b * a.h_q);
+  const int qb = n_qblk - 1 - blockIdx.x / (a.b * a.h_q);
+  const int bi = bh / a.h_q, hq = bh % a.h_q;
+  const int g = hq / (a.h_q / a.h_kv);
+  const int qblk0 = qb * 64;
+  const int my_q = qblk0 + tid;
+  const float* qp = (const float*)a.q + bi * a.qs.b + hq * a.qs.h;
+  const float* kp = (const float*)a.k + bi * a.ks.b + g * a.ks.h;
+  const float* vp = (const float*)a.v + bi * a.vs.b + g * a.vs.h;
+  const float sl2 = a.scale * kLog2e;
+
+  float qv[D], o[D];
+#pragma unroll
+  for (int d4 = 0; d4 < D; d4 += 4) {
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (my_q < a.s_q) x = *(const f32x4*)(qp + (int64_t)my_q * a.qs.s + d4);
+    qv[d4] = x[0] * sl2;
+    qv[d4 + 1] = x[1] * sl2;
+    qv[d4 + 2] = x[2] * sl2;
+    qv[d4 + 3] = x[3] * sl2;
+    o[d4] = o[d4 + 1] = o[d4 + 2] = o[d4 + 3] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + 64) : a.s_kv;
+  for (int k0 = 0; k0 < kv_end; k0 += BN) {
+    __syncthreads();
+    for (int c = tid; c < BN * D / 4; c += 64) {
+      const int r = c / (D / 4), d4 = 4 * (c % (D / 4));
+      f32x4 kx = f32x4{0.f, 0.f, 0.f, 0.f}, vx = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k0 + r < a.s_kv) {
+        kx = *(const f32x4*)(kp + (int64_t)(k0 + r) * a.ks.s + d4);
+        vx = *(const f32x4*)(vp + (int64_t)(k0 + r) * a.vs.s + d4);
+      }
+      *(f32x4*)(&Ks[r * D + d4]) = kx;
+      *(f32x4*)(&Vs[r * D + d4]) = vx;
+    }
+    __syncthreads();
+    float s[BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      float acc = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) acc = fmaf(qv[dd], Ks[jj * D + dd], acc);
+      const int key = k0 + jj;
+      if (key >= a.s_kv || (CAUSAL && key > my_q)) acc = -INFINITY;
+      s[jj] = acc;
+      mx = fmaxf(mx, acc);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) o[dd] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      const float p = __builtin_amdgcn_exp2f(s[jj] - m_new);
+      l_run += p;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) o[dd] = fmaf(p, Vs[jj * D + dd], o[dd]);
+    }
+  }
+  if (my_q < a.s_q) {
+    const float inv = 1.f / l_run;
+    float* op = (float*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
+#pragma unroll
+    for (int d4 = 0; d4 < D; d4 += 4)
+      *(f32x4*)(op + d4) = f32x4{o[d4] * inv, o[d4 + 1] * inv, o[d4 + 2] * inv, o[d4 + 3] * inv};
+    if (a.lse != nullptr) a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
+  const int n_qblk = (a.s_q + kBM - 1) / kBM;
+  const dim3 grid(n_qblk * a.b * a.h_q), block(256);
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), grid, block, 0, stream, a, n_qblk);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false>), grid, block, 0, stream, a, n_qblk);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
+  const int n_qblk = (a.s_q + 63) / 64;
+  const dim3 grid(n_qblk * a.b * a.h_q), block(64);
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, block, 0, stream, a, n_qblk);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, block, 0, stream, a, n_qblk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream) {
+  if (io == Io::BF16) return a.d == 64 ? launch_mfma_d<Bf16T, 64>(a, stream) : launch_mfma_d<Bf16T, 128>(a, stream);
+  return a.d == 64 ? launch_mfma_d<F16T, 64>(a, stream) : launch_mfma_d<F16T, 128>(a, stream);
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch_f32_d<64>(a, stream) : launch_f32_d<128>(a, stream);
+}
+
+}  // namespace sdpa

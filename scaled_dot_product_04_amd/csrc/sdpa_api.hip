@@ -1,0 +1,279 @@
+// C-ABI front end: argument validation, kernel choice, launch, error state.
+//
+// Follows the execution flow of "Using cuDNN in Python" (tensor descriptors
+// with dims + strides, a support check before execution, execute(pointers,
+// workspace) on a stream, caller-side synchronisation) and the error
+// reporting of the cuDNN 9 blog ("Improved error reporting": specific codes
+// plus a programmatic last-error string). Unsupported problems are reported,
+// never silently run on another path (the JAX attention codelab's step 6:
+// forcing a backend raises instead of falling back).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/sdpa.h"
+#include "sdpa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local sdpa::TimingEvents g_timing{};
+
+int log_level() {
+  static int level = [] {
+    const char* s = getenv("SDPA_LOG_LEVEL");
+    return s ? atoi(s) : 0;
+  }();
+  return level;
+}
+
+sdpa_status_t fail(sdpa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  if (log_level() >= 1) fprintf(stderr, "[sdpa] %s: %s\n", sdpa_status_string(st), buf);
+  return st;
+}
+
+int elem_bytes(sdpa_dtype_t t) {
+  switch (t) {
+    case SDPA_F32: return 4;
+    case SDPA_F16:
+    case SDPA_BF16: return 2;
+    case SDPA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool valid_dtype(int t) { return t >= SDPA_F32 && t <= SDPA_FP8_E4M3; }
+
+// Checks one tensor's pointer and strides. Returns SDPA_OK or an error.
+sdpa_status_t check_tensor(const char* name, const void* p, const int64_t* st, int eb,
+                           sdpa::Strides3* out) {
+  if (p == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (st == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s stride array is NULL", name);
+  if (st[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s d-stride is %lld, must be 1", name, (long long)st[3]);
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s stride[%d] is negative", name, i);
+  if (((uintptr_t)p) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i)
+    if ((st[i] * eb) % 16 != 0)
+      return fail(SDPA_ERR_NOT_SUPPORTED, "%s stride[%d]=%lld is not a multiple of 16 bytes", name, i,
+                  (long long)st[i]);
+  out->b = st[0];
+  out->h = st[1];
+  out->s = st[2];
+  return SDPA_OK;
+}
+
+sdpa_status_t check_sizes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
+  if (b < 0 || s_q < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "b=%d and s_q=%d must be >= 0", b, s_q);
+  if (h_q < 1 || h_kv < 1 || s_kv < 1 || d < 1)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "h_q=%d, h_kv=%d, s_kv=%d, d=%d must be >= 1", h_q, h_kv, s_kv, d);
+  if (h_q % h_kv != 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  // grid size: query blocks x b x h_q must fit a 32-bit grid
+  if ((int64_t)((s_q + 31) / 32) * b * h_q > 0x7fffffffLL)
+    return fail(SDPA_ERR_NOT_SUPPORTED, "problem too large for one launch");
+  return SDPA_OK;
+}
+
+sdpa_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdpa_status_string(sdpa_status_t s) {
+  switch (s) {
+    case SDPA_OK: return "SDPA_OK";
+    case SDPA_ERR_INVALID_ARGUMENT: return "SDPA_ERR_INVALID_ARGUMENT";
+    case SDPA_ERR_NOT_SUPPORTED: return "SDPA_ERR_NOT_SUPPORTED";
+    case SDPA_ERR_WORKSPACE_TOO_SMALL: return "SDPA_ERR_WORKSPACE_TOO_SMALL";
+    case SDPA_ERR_HIP: return "SDPA_ERR_HIP";
+  }
+  return "SDPA_ERR_UNKNOWN";
+}
+
+const char* sdpa_last_error(void) { return g_last_error.c_str(); }
+
+sdpa_status_t sdpa_set_timing_events(hipEvent_t* events, int n) {
+  g_last_error.clear();
+  if (n < 0 || n > 8 || (n > 0 && events == nullptr))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "timing events: n=%d must be in [0, 8] with a non-NULL array", n);
+  g_timing.n = events == nullptr ? 0 : n;
+  for (int i = 0; i < g_timing.n; ++i) g_timing.ev[i] = events[i];
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
+                       int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                       const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
+                       float attn_scale, int causal, sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
+                       const sdpa_fp8_scales_t* fp8, hipStream_t stream) {
+  g_last_error.clear();
+  sdpa_status_t st;
+  if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype (%d, %d)", (int)in_dtype, (int)out_dtype);
+  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (!(attn_scale > 0.f) || !isfinite(attn_scale))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
+  if ((in_dtype == SDPA_FP8_E4M3) != (fp8 != nullptr))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 scales must be given iff in_dtype is FP8_E4M3");
+  if (fp8 != nullptr) {
+    const float f[5] = {fp8->descale_q, fp8->descale_k, fp8->descale_v, fp8->scale_p, fp8->descale_p};
+    for (float x : f)
+      if (!(x > 0.f) || !isfinite(x)) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 factors must be finite and > 0");
+  }
+  sdpa::Io io;
+  bool ok = false;
+  if (in_dtype == SDPA_F32 && out_dtype == SDPA_F32) {
+    io = sdpa::Io::F32;
+    ok = d == 64 || d == 128;
+  } else if (in_dtype == SDPA_F16 && out_dtype == SDPA_F16) {
+    io = sdpa::Io::F16;
+    ok = d == 64 || d == 128;
+  } else if (in_dtype == SDPA_BF16 && out_dtype == SDPA_BF16) {
+    io = sdpa::Io::BF16;
+    ok = d == 64 || d == 128;
+  } else if (in_dtype == SDPA_FP8_E4M3 && out_dtype == SDPA_BF16) {
+    io = sdpa::Io::FP8;
+    ok = false;  // fp8 kernel not built yet
+  }
+  if (!ok)
+    return fail(SDPA_ERR_NOT_SUPPORTED, "no forward kernel for in=%d out=%d d=%d", (int)in_dtype, (int)out_dtype, d);
+
+  // Empty problem: nothing to compute or write; the (possibly NULL) pointers of
+  // empty tensors are not inspected.
+  if (b == 0 || s_q == 0) return SDPA_OK;
+  sdpa::FwdArgs a{};
+  const int ein = elem_bytes(in_dtype), eout = elem_bytes(out_dtype);
+  if ((st = check_tensor("q", q, q_stride, ein, &a.qs)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, ein, &a.ks)) != SDPA_OK) return st;
+  if ((st = check_tensor("v", v, v_stride, ein, &a.vs)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, eout, &a.os)) != SDPA_OK) return st;
+  if (lse != nullptr && ((uintptr_t)lse) % 4 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "lse is not 4-byte aligned");
+
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.b = b;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.s_q = s_q;
+  a.s_kv = s_kv;
+  a.d = d;
+  a.causal = causal;
+  a.scale = attn_scale;
+  if (fp8 != nullptr) {
+    a.scale = attn_scale * fp8->descale_q * fp8->descale_k;
+    a.descale_v = fp8->descale_v;
+    a.scale_p = fp8->scale_p;
+    a.descale_p = fp8->descale_p;
+  }
+  if (log_level() >= 2)
+    fprintf(stderr, "[sdpa] fwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d causal=%d\n", (int)io, d, b, h_q,
+            h_kv, s_q, s_kv, causal);
+  if (g_timing.n >= 2) (void)hipEventRecord(g_timing.ev[0], stream);
+  hipError_t e;
+  switch (io) {
+    case sdpa::Io::F32: e = sdpa::launch_fwd_f32(a, stream); break;
+    default: e = sdpa::launch_fwd_mfma(a, io, stream); break;
+  }
+  if (e == hipSuccess && g_timing.n >= 2) e = hipEventRecord(g_timing.ev[1], stream);
+  return hip_status(e, "forward launch");
+}
+
+size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d, int causal,
+                               sdpa_dtype_t dtype) {
+  (void)causal;
+  (void)dtype;
+  if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_kv <= 0 || d <= 0) return 0;
+  return sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
+}
+
+sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int b, int h_q, int h_kv, int s_q,
+                       int s_kv, int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                       const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+                       const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4],
+                       float attn_scale, int causal, sdpa_dtype_t dtype, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  sdpa_status_t st;
+  if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
+  if (!valid_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (!(attn_scale > 0.f) || !isfinite(attn_scale))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
+  if (!((dtype == SDPA_BF16 || dtype == SDPA_F16) && (d == 64 || d == 128)))
+    return fail(SDPA_ERR_NOT_SUPPORTED, "no backward kernel for dtype=%d d=%d", (int)dtype, d);
+  sdpa::BwdArgs a{};
+  const int eb = elem_bytes(dtype);
+  const sdpa::Io io = dtype == SDPA_BF16 ? sdpa::Io::BF16 : sdpa::Io::F16;
+  if (b == 0) return SDPA_OK;  // empty problem: every tensor is empty
+  if (s_q == 0) {
+    // No query rows: dK = dV = 0; only those two tensors are touched.
+    if ((st = check_tensor("dk", dk, dk_stride, eb, &a.dks)) != SDPA_OK) return st;
+    if ((st = check_tensor("dv", dv, dv_stride, eb, &a.dvs)) != SDPA_OK) return st;
+    a.dk = dk;
+    a.dv = dv;
+    a.b = b;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.s_kv = s_kv;
+    a.d = d;
+    return hip_status(sdpa::launch_zero_dkdv(a, io, stream), "zero dK/dV launch");
+  }
+  if (lse == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse is required by the backward");
+  if ((st = check_tensor("q", q, q_stride, eb, &a.qs)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, eb, &a.ks)) != SDPA_OK) return st;
+  if ((st = check_tensor("v", v, v_stride, eb, &a.vs)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, eb, &a.os)) != SDPA_OK) return st;
+  if ((st = check_tensor("dout", dout, do_stride, eb, &a.dos)) != SDPA_OK) return st;
+  if ((st = check_tensor("dq", dq, dq_stride, eb, &a.dqs)) != SDPA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_stride, eb, &a.dks)) != SDPA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_stride, eb, &a.dvs)) != SDPA_OK) return st;
+  if (((uintptr_t)lse) % 4 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "lse is not 4-byte aligned");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.b = b;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.s_q = s_q;
+  a.s_kv = s_kv;
+  a.d = d;
+  a.causal = causal;
+  a.scale = attn_scale;
+  const size_t need = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  if (workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (workspace == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)workspace) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "workspace is not 16-byte aligned");
+  a.delta = (float*)workspace;
+  if (log_level() >= 2)
+    fprintf(stderr, "[sdpa] bwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d causal=%d\n", (int)io, d, b, h_q,
+            h_kv, s_q, s_kv, causal);
+  return hip_status(sdpa::launch_bwd(a, io, stream, g_timing), "backward launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI front end (sdpa_api.hip) and the
+// kernel files. Not installed; not part of the public header.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace sdpa {
+
+// Element strides (b, h, s) of one logical (b, h, s, d) tensor; d stride is 1.
+struct Strides3 {
+  int64_t b, h, s;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  Strides3 qs, ks, vs, os;
+  int b, h_q, h_kv, s_q, s_kv, d;
+  int causal;
+  float scale;  // attn_scale (already multiplied by the fp8 q/k descales for fp8)
+  // fp8 only
+  float descale_v, scale_p, descale_p;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  Strides3 qs, ks, vs, os, dos, dqs, dks, dvs;
+  int b, h_q, h_kv, s_q, s_kv, d;
+  int causal;
+  float scale;
+  float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
+};
+
+// Caller events recorded at kernel boundaries (timing hook); n = 0 disables.
+struct TimingEvents {
+  hipEvent_t ev[8];
+  int n;
+};
+
+enum class Io { F32, F16, BF16, FP8 };
+
+// Kernel launchers; each returns hipGetLastError() after enqueueing.
+hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te);
+hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
+
+// Workspace bytes the backward needs (see sdpa_bwd_workspace_size).
+size_t bwd_workspace_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d);
+
+}  // namespace sdpa

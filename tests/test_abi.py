@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sdpa.h declares, and rejects invalid arguments before launching
+anything (every call here fails validation, so no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_04_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced: every call below fails validation
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = sdpa.load_library()
+    names = _declared_functions()
+    assert {"sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_last_error",
+            "sdpa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = sdpa.load_library()
+    for code, name in sdpa.STATUS_NAMES.items():
+        assert lib.sdpa_status_string(code).decode() == name
+
+
+def _bshd(b, h, s, d):
+    return (s * h * d, d, h * d, 1)
+
+
+def _fwd(**kw):
+    lib = sdpa.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, b=2, h_q=4, h_kv=2, s_q=64, s_kv=64, d=128,
+             qs=_bshd(2, 4, 64, 128), ks=_bshd(2, 2, 64, 128), vs=_bshd(2, 2, 64, 128),
+             os=_bshd(2, 4, 64, 128), scale=0.088, causal=1, tin=sdpa.SDPA_BF16, tout=sdpa.SDPA_BF16,
+             fp8=None)
+    a.update(kw)
+    S = ctypes.c_int64 * 4
+    st = lib.sdpa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"], a["h_q"], a["h_kv"], a["s_q"],
+                      a["s_kv"], a["d"], S(*a["qs"]), S(*a["ks"]), S(*a["vs"]), S(*a["os"]), a["scale"],
+                      a["causal"], a["tin"], a["tout"], a["fp8"], None)
+    return st, lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(h_q=6, h_kv=4), 1, "multiple"),
+    (dict(h_kv=0), 1, ">= 1"),
+    (dict(s_kv=0), 1, ">= 1"),
+    (dict(d=0), 1, ">= 1"),
+    (dict(b=-1), 1, ">= 0"),
+    (dict(causal=2), 1, "causal"),
+    (dict(scale=0.0), 1, "attn_scale"),
+    (dict(scale=float("nan")), 1, "attn_scale"),
+    (dict(scale=-0.1), 1, "attn_scale"),
+    (dict(qs=(0, 0, 0, 2)), 1, "d-stride"),
+    (dict(tin=7), 1, "dtype"),
+    (dict(d=96, qs=_bshd(2, 4, 64, 96)), 2, "no forward kernel"),
+    (dict(tin=sdpa.SDPA_BF16, tout=sdpa.SDPA_F16), 2, "no forward kernel"),
+    (dict(q=FAKE + 2), 2, "16-byte aligned"),
+    (dict(ks=(64 * 2 * 128, 128, 2 * 128 + 4, 1)), 2, "multiple of 16 bytes"),
+    (dict(tin=sdpa.SDPA_FP8_E4M3), 1, "fp8 scales"),
+])
+def test_forward_validation_errors(kw, status, needle):
+    st, msg = _fwd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_forward_empty_problem_is_a_no_op():
+    # b == 0: valid, nothing to compute, nothing enqueued
+    st, msg = _fwd(b=0)
+    assert st == 0 and msg == ""
+    st, msg = _fwd(s_q=0)
+    assert st == 0
+
+
+def _bwd(**kw):
+    lib = sdpa.load_library()
+    b, hq, hkv, s, d = 2, 4, 2, 64, 128
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, b=b, h_q=hq,
+             h_kv=hkv, s_q=s, s_kv=s, d=d, scale=0.088, causal=1, dtype=sdpa.SDPA_BF16, ws=FAKE,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    S = ctypes.c_int64 * 4
+    qs, ks = S(*_bshd(b, hq, s, d)), S(*_bshd(b, hkv, s, d))
+    st = lib.sdpa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                      a["b"], a["h_q"], a["h_kv"], a["s_q"], a["s_kv"], a["d"], qs, ks, ks, qs, qs, qs, ks,
+                      ks, a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"], None)
+    return st, lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), 1, "lse is required"),
+    (dict(dq=None), 1, "dq is NULL"),
+    (dict(h_q=3), 1, "multiple"),
+    (dict(dtype=sdpa.SDPA_F32), 2, "no backward kernel"),
+    (dict(dtype=sdpa.SDPA_FP8_E4M3), 2, "no backward kernel"),
+    (dict(d=256), 2, "no backward kernel"),
+    (dict(ws_bytes=16), 3, "workspace"),
+    (dict(dk=FAKE + 8), 2, "16-byte aligned"),
+])
+def test_backward_validation_errors(kw, status, needle):
+    st, msg = _bwd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_workspace_size_is_positive_and_monotone():
+    f = sdpa.load_library().sdpa_bwd_workspace_size
+    small = f(1, 4, 4, 128, 128, 128, 1, sdpa.SDPA_BF16)
+    big = f(2, 16, 16, 8192, 8192, 128, 1, sdpa.SDPA_BF16)
+    assert 0 < small < big
+    assert small % 16 == 0 and big % 16 == 0
+    assert f(0, 4, 4, 128, 128, 128, 1, sdpa.SDPA_BF16) == 0
