@@ -80,67 +80,104 @@ __global__ __launch_bounds__(256) void zero_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// Stages rows [row0, row0 + R) x D of a 16-bit tensor (rows >= n_rows are
-// zero) into LDS twice: row-major (stride D + 8) and transposed (stride R + 4),
-// via 4x4 blocks loaded as 8-byte row pieces.
+// A tile of R rows x D 16-bit elements in flight in registers, as 4x4
+// blocks (row group rg, column group dg). Each 16-lane group covers 4 column
+// groups x 4 row groups, so the transposed LDS writes of a group fall in
+// distinct banks and each row segment read from HBM is 128 B (d = 128).
+// Loads are raw buffer loads from a per-tile descriptor; rows past the end of
+// the tensor read as zero. Byte offsets inside a tile are loop-invariant.
+// From registers the tile is written to LDS row-major (row stride D + 8)
+// and/or transposed (row stride R + 4, one row per column of the tile).
 template <int R, int D>
-__device__ __forceinline__ void stage_both(const uint16_t* src, int64_t row_stride, int row0, int n_rows,
-                                           uint16_t* rm, uint16_t* tr, int tid) {
-  constexpr int DG = D / 4;
-  constexpr int RS = D + 8, TS = R + 4;
-#pragma unroll
-  for (int c = tid; c < (R / 4) * DG; c += 256) {
-    const int dg = c % DG, rg = c / DG;
-    u32x2 rows[4], cols[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * rg + r;
-      rows[r] = u32x2{0, 0};
-      if (row < n_rows) rows[r] = *(const u32x2*)(src + (int64_t)row * row_stride + 4 * dg);
-      *(u32x2*)(&rm[(4 * rg + r) * RS + 4 * dg]) = rows[r];
-    }
-    transpose4x4_b16(rows, cols);
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&tr[(4 * dg + c2) * TS + 4 * rg]) = cols[c2];
-  }
-}
+struct BlockTile {
+  static constexpr int DG = D / 4;
+  static constexpr int TOTAL = (R / 4) * DG;
+  static constexpr int NB = (TOTAL + 255) / 256;
+  static constexpr int RS = D + 8, TS = R + 4;
+  static_assert(DG % 4 == 0 && (R / 4) % 4 == 0, "block map needs 4x4 groups");
+  u32x2 v[NB][4];
+  uint32_t off[NB];   // byte offset of the block's first row
+  uint32_t rm_dst[NB], tr_dst[NB];
+  int64_t stride;
 
-// Stages rows [row0, row0 + R) x D row-major (stride D + 8), zero beyond n_rows.
-template <int R, int D>
-__device__ __forceinline__ void stage_rm(const uint16_t* src, int64_t row_stride, int row0, int n_rows,
-                                         uint16_t* rm, int tid) {
-  constexpr int CH = D / 8;
-  constexpr int RS = D + 8;
+  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
+    stride = row_stride;
 #pragma unroll
-  for (int c = tid; c < R * CH; c += 256) {
-    const int r = c / CH, cc = c - (c / CH) * CH;
-    u32x4 val = u32x4{0, 0, 0, 0};
-    if (row0 + r < n_rows) val = *(const u32x4*)(src + (int64_t)(row0 + r) * row_stride + cc * 8);
-    *(u32x4*)(&rm[r * RS + cc * 8]) = val;
-  }
-}
-
-// Stages rows [row0, row0 + R) x D transposed (stride R + 4), zero beyond n_rows.
-template <int R, int D>
-__device__ __forceinline__ void stage_tr(const uint16_t* src, int64_t row_stride, int row0, int n_rows,
-                                         uint16_t* tr, int tid) {
-  constexpr int DG = D / 4;
-  constexpr int TS = R + 4;
-#pragma unroll
-  for (int c = tid; c < (R / 4) * DG; c += 256) {
-    const int dg = c % DG, rg = c / DG;
-    u32x2 rows[4], cols[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * rg + r;
-      rows[r] = u32x2{0, 0};
-      if (row < n_rows) rows[r] = *(const u32x2*)(src + (int64_t)row * row_stride + 4 * dg);
+    for (int i = 0; i < NB; ++i) {
+      const int c = tid + 256 * i;
+      const int sub = c & 15, grp = c >> 4;
+      const int dg = (sub & 3) + 4 * (grp % (DG / 4));
+      const int rg = (sub >> 2) + 4 * (grp / (DG / 4));
+      off[i] = (uint32_t)((4 * rg) * row_stride * 2 + 8 * dg);
+      rm_dst[i] = (4 * rg) * RS + 4 * dg;
+      tr_dst[i] = (4 * dg) * TS + 4 * rg;
     }
-    transpose4x4_b16(rows, cols);
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&tr[(4 * dg + c2) * TS + 4 * rg]) = cols[c2];
   }
-}
+  __device__ __forceinline__ bool active(int i, int tid) const { return TOTAL % 256 == 0 || tid + 256 * i < TOTAL; }
+  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows, int tid) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
+    const uint32_t rstep = (uint32_t)(stride * 2);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (!active(i, tid)) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[i][r] = buf_load8(rs, off[i] + r * rstep);
+    }
+  }
+  __device__ __forceinline__ void store_rm(uint16_t* rm, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (!active(i, tid)) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *(u32x2*)(&rm[rm_dst[i] + r * RS]) = v[i][r];
+    }
+  }
+  __device__ __forceinline__ void store_tr(uint16_t* tr, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (!active(i, tid)) continue;
+      u32x2 cols[4];
+      transpose4x4_b16(v[i], cols);
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&tr[tr_dst[i] + c2 * TS]) = cols[c2];
+    }
+  }
+};
+
+// A tile of R rows x D 16-bit elements in flight as 16-byte row chunks,
+// written to LDS row-major (row stride D + 8). Buffer loads as above.
+template <int R, int D>
+struct ChunkTile {
+  static constexpr int CH = D / 8;
+  static constexpr int NC = R * CH / 256;
+  static constexpr int RS = D + 8;
+  static_assert(NC * 256 == R * CH, "tile / thread mismatch");
+  u32x4 v[NC];
+  uint32_t off[NC], dst[NC];
+  int64_t stride;
+
+  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
+    stride = row_stride;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CH, cc = c % CH;
+      off[i] = (uint32_t)(r * row_stride * 2 + cc * 16);
+      dst[i] = r * RS + cc * 8;
+    }
+  }
+  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows, int tid) {
+    (void)tid;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) v[i] = buf_load16(rs, off[i]);
+  }
+  __device__ __forceinline__ void store(uint16_t* rm, int tid) const {
+    (void)tid;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) *(u32x4*)(&rm[dst[i]]) = v[i];
+  }
+};
 
 // A operand taken from a transposed LDS tile (row = feature index f, stride TS):
 // lane half h element m stands for row key_of(t, h, m) of the original tile.
@@ -155,17 +192,21 @@ __device__ __forceinline__ V8 read_tr_operand(const uint16_t* tr, int TS, int f,
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
+// The workgroup walks (query head of its group slice, query tile) pairs in
+// order; the Q / dO tile of step it+2 is loaded into registers while step it
+// is computed, and written to the other LDS buffer at step it+1.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk, int n_split, float* part) {
   typedef typename T::vec8 V8;
+  typedef BlockTile<kQTile, D> QTile;
   constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int RS = D + 8, TS = kQTile + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kQTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds_[kQTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[D * TS];
-  __shared__ __attribute__((aligned(16))) float lse2s[kQTile];
-  __shared__ __attribute__((aligned(16))) float dels[kQTile];
+  constexpr int RS = QTile::RS, TS = QTile::TS;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kQTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds_[2][kQTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TS];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][kQTile];
+  __shared__ __attribute__((aligned(16))) float dels[2][kQTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -208,70 +249,101 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
   const float sl2 = a.scale * kLog2e;
   const int n_qt = (a.s_q + kQTile - 1) / kQTile;
-  const int qt0 = CAUSAL ? (kb * kKvBlock) / kQTile : 0;
+  const int qt0 = CAUSAL ? min(n_qt, (kb * kKvBlock) / kQTile) : 0;
+  const int nq = n_qt - qt0;
+  const int n_it = Gs * nq;
+  const int hq_base = g * G + sp * Gs;
 
-  for (int hi = 0; hi < Gs; ++hi) {
-    const int hq = g * G + sp * Gs + hi;
+  QTile qreg, dreg;
+  qreg.init(a.qs.s, tid);
+  dreg.init(a.dos.s, tid);
+  float lreg = 0.f, creg = 0.f;
+  auto load_tile = [&](int it) {
+    const int hq = hq_base + it / nq;
+    const int q0 = (qt0 + it % nq) * kQTile;
     const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h;
     const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h;
-    const float* lsep = a.lse + ((int64_t)bi * a.h_q + hq) * a.s_q;
-    const float* delp = a.delta + ((int64_t)bi * a.h_q + hq) * a.s_q;
-    for (int qt = qt0; qt < n_qt; ++qt) {
-      const int q0 = qt * kQTile;
-      __syncthreads();
-      stage_both<kQTile, D>(qp, a.qs.s, q0, a.s_q, Qs, Qt, tid);
-      stage_both<kQTile, D>(dop, a.dos.s, q0, a.s_q, Ds_, Dt, tid);
-      if (tid < kQTile) {
-        const int qi = q0 + tid;
-        lse2s[tid] = qi < a.s_q ? lsep[qi] * kLog2e : 0.f;
-        dels[tid] = qi < a.s_q ? delp[qi] : 0.f;
-      }
-      __syncthreads();
-      if (CAUSAL && q0 + kQTile - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    qreg.load(qp, q0, a.s_q, tid);
+    dreg.load(dop, q0, a.s_q, tid);
+    if (tid < kQTile) {
+      const int qi = q0 + tid;
+      const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + qi;
+      lreg = qi < a.s_q ? a.lse[row] * kLog2e : 0.f;
+      creg = qi < a.s_q ? a.delta[row] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    qreg.store_rm(Qs[buf], tid);
+    qreg.store_tr(Qt[buf], tid);
+    dreg.store_rm(Ds_[buf], tid);
+    dreg.store_tr(Dt[buf], tid);
+    if (tid < kQTile) {
+      lse2s[buf][tid] = lreg;
+      dels[buf][tid] = creg;
+    }
+  };
 
-      // S = Q K^T and dP = dO V^T for 32 queries x this lane's key.
-      f32x16 s = f32x16{}, dp = f32x16{};
+  if (n_it > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_it > 1) load_tile(1);
+  }
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    const int q0 = (qt0 + it % nq) * kQTile;
+    __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
+    if (it + 1 < n_it) {
+      store_tile(buf ^ 1);
+      if (it + 2 < n_it) load_tile(it + 2);
+    }
+    if (CAUSAL && q0 + kQTile - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+
+    // S = Q K^T and dP = dO V^T for 32 queries x this lane's key.
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        const V8 qa = *(const V8*)(&Qs[j * RS + 16 * t + 8 * h]);
-        s = T::mfma(qa, kf[t], s);
-        const V8 da = *(const V8*)(&Ds_[j * RS + 16 * t + 8 * h]);
-        dp = T::mfma(da, vf[t], dp);
-      }
-      // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
-      uint32_t ppk[8], dspk[8];
+    for (int t = 0; t < NKS; ++t) {
+      const V8 qa = *(const V8*)(&Qs[buf][j * RS + 16 * t + 8 * h]);
+      s = T::mfma(qa, kf[t], s);
+      const V8 da = *(const V8*)(&Ds_[buf][j * RS + 16 * t + 8 * h]);
+      dp = T::mfma(da, vf[t], dp);
+    }
+    // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
+    const bool need_mask = CAUSAL ? (q0 < kw0 + 31 || q0 + kQTile > a.s_q) : (q0 + kQTile > a.s_q);
+    uint32_t ppk[8], dspk[8];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int row0 = 8 * r4 + 4 * h;
-        const f32x4 l4 = *(const f32x4*)(&lse2s[row0]);
-        const f32x4 d4 = *(const f32x4*)(&dels[row0]);
-        float pv[4], dsv[4];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row0 = 8 * r4 + 4 * h;
+      const f32x4 l4 = *(const f32x4*)(&lse2s[buf][row0]);
+      const f32x4 d4 = *(const f32x4*)(&dels[buf][row0]);
+      float pv[4], dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e) {
+        float x = s[4 * r4 + e];
+        if (need_mask) {
           const int qi = q0 + row0 + e;
-          const bool ok = qi < a.s_q && my_key < a.s_kv && (!CAUSAL || my_key <= qi);
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, -l4[e])) : 0.f;
-          pv[e] = p;
-          dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
+          if (qi >= a.s_q || (CAUSAL && my_key > qi)) x = -INFINITY;
         }
-        ppk[2 * r4] = pack2<T>(pv[0], pv[1]);
-        ppk[2 * r4 + 1] = pack2<T>(pv[2], pv[3]);
-        dspk[2 * r4] = pack2<T>(dsv[0], dsv[1]);
-        dspk[2 * r4 + 1] = pack2<T>(dsv[2], dsv[3]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, -l4[e]));
+        pv[e] = p;
+        dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
+      ppk[2 * r4] = pack2<T>(pv[0], pv[1]);
+      ppk[2 * r4 + 1] = pack2<T>(pv[2], pv[3]);
+      dspk[2 * r4] = pack2<T>(dsv[0], dsv[1]);
+      dspk[2 * r4 + 1] = pack2<T>(dsv[2], dsv[3]);
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
 #pragma unroll
-      for (int t2 = 0; t2 < kQTile / 16; ++t2) {
-        const V8 pb = __builtin_bit_cast(V8, u32x4{ppk[4 * t2], ppk[4 * t2 + 1], ppk[4 * t2 + 2], ppk[4 * t2 + 3]});
-        const V8 sb =
-            __builtin_bit_cast(V8, u32x4{dspk[4 * t2], dspk[4 * t2 + 1], dspk[4 * t2 + 2], dspk[4 * t2 + 3]});
+    for (int t2 = 0; t2 < kQTile / 16; ++t2) {
+      const V8 pb = __builtin_bit_cast(V8, u32x4{ppk[4 * t2], ppk[4 * t2 + 1], ppk[4 * t2 + 2], ppk[4 * t2 + 3]});
+      const V8 sb =
+          __builtin_bit_cast(V8, u32x4{dspk[4 * t2], dspk[4 * t2 + 1], dspk[4 * t2 + 2], dspk[4 * t2 + 3]});
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const V8 doa = read_tr_operand<V8>(Dt, TS, db * 32 + j, t2, h);
-          dv[db] = T::mfma(doa, pb, dv[db]);
-          const V8 qta = read_tr_operand<V8>(Qt, TS, db * 32 + j, t2, h);
-          dk[db] = T::mfma(qta, sb, dk[db]);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        const V8 doa = read_tr_operand<V8>(Dt[buf], TS, db * 32 + j, t2, h);
+        dv[db] = T::mfma(doa, pb, dv[db]);
+        const V8 qta = read_tr_operand<V8>(Qt[buf], TS, db * 32 + j, t2, h);
+        dk[db] = T::mfma(qta, sb, dk[db]);
       }
     }
   }
@@ -336,14 +408,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split,
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
+// Pipelined like the forward: the K/V tile of step t+2 is loaded into
+// registers while step t is computed and written to the other LDS buffer
+// (K row-major and transposed, V row-major) at step t+1.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   typedef typename T::vec8 V8;
+  typedef BlockTile<kKTile, D> KTile;
+  typedef ChunkTile<kKTile, D> VTile;
   constexpr int NKS = D / 16, NDB = D / 32, NSB = kKTile / 32;
-  constexpr int RS = D + 8, TS = kKTile + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kKTile * RS];
+  constexpr int RS = KTile::RS, TS = KTile::TS;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile * RS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -388,13 +465,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
 
   const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + kQBlock) : a.s_kv;
   const int n_tiles = (kv_end + kKTile - 1) / kKTile;
+  KTile kreg;
+  VTile vreg;
+  kreg.init(a.ks.s, tid);
+  vreg.init(a.vs.s, tid);
+  auto load_tile = [&](int k0) {
+    kreg.load(kp, k0, a.s_kv, tid);
+    vreg.load(vp, k0, a.s_kv, tid);
+  };
+  auto store_tile = [&](int buf) {
+    kreg.store_rm(Ks[buf], tid);
+    kreg.store_tr(Kt[buf], tid);
+    vreg.store(Vs[buf], tid);
+  };
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(kKTile);
+  }
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int k0 = tile * kKTile;
-    __syncthreads();
-    stage_rm<kKTile, D>(kp, a.ks.s, k0, a.s_kv, Ks, tid);
-    stage_tr<kKTile, D>(kp, a.ks.s, k0, a.s_kv, Kt, tid);
-    stage_rm<kKTile, D>(vp, a.vs.s, k0, a.s_kv, Vs, tid);
-    __syncthreads();
+    const int buf = tile & 1;
+    __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
+    if (tile + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      if (tile + 2 < n_tiles) load_tile((tile + 2) * kKTile);
+    }
     if (CAUSAL && k0 > q0 + 31) continue;
 
     f32x16 s[NSB], dp[NSB];
@@ -404,9 +500,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       dp[nb] = f32x16{};
 #pragma unroll
       for (int t = 0; t < NKS; ++t) {
-        const V8 ka = *(const V8*)(&Ks[(nb * 32 + j) * RS + 16 * t + 8 * h]);
+        const V8 ka = *(const V8*)(&Ks[buf][(nb * 32 + j) * RS + 16 * t + 8 * h]);
         s[nb] = T::mfma(ka, qf[t], s[nb]);
-        const V8 va = *(const V8*)(&Vs[(nb * 32 + j) * RS + 16 * t + 8 * h]);
+        const V8 va = *(const V8*)(&Vs[buf][(nb * 32 + j) * RS + 16 * t + 8 * h]);
         dp[nb] = T::mfma(va, df[t], dp[nb]);
       }
     }
@@ -437,7 +533,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
           V8, u32x4{dspk[nb][base], dspk[nb][base + 1], dspk[nb][base + 2], dspk[nb][base + 3]});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const V8 kta = read_tr_operand<V8>(Kt, TS, db * 32 + j, t2, h);
+        const V8 kta = read_tr_operand<V8>(Kt[buf], TS, db * 32 + j, t2, h);
         dq[db] = T::mfma(kta, sb, dq[db]);
       }
     }

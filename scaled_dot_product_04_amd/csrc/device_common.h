@@ -47,13 +47,44 @@ struct F16T {
   }
 };
 
-// Two fp32 values rounded to nearest-even 16-bit and packed (low = x).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even 16-bit and packed (low = x); one
+// v_cvt_pk_{bf16,f16}_f32.
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
   typedef typename T::elem E;
-  E ex = (E)x, ey = (E)y;
-  uint16_t ux = __builtin_bit_cast(uint16_t, ex), uy = __builtin_bit_cast(uint16_t, ey);
-  return (uint32_t)ux | ((uint32_t)uy << 16);
+  typedef E E2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), E2));
+}
+
+// Buffer resource for raw buffer loads of gfx9-class GPUs: `bytes` is the
+// number of addressable bytes from `base`; loads at offsets >= bytes return 0.
+// Base and size must be the same in every lane of the wave (they are read
+// from the first lane, so the descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* up = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Bytes of rows [row0, n_rows) of a row-major tile with `row_stride` elements
+// between rows and `row_len` elements per row (0 if none), clamped to 2^31.
+__device__ __forceinline__ uint32_t tile_bytes(int row0, int n_rows, int64_t row_stride, int row_len,
+                                               int elem_bytes) {
+  if (row0 >= n_rows) return 0u;
+  const int64_t b = ((int64_t)(n_rows - row0 - 1) * row_stride + row_len) * elem_bytes;
+  return b > 0x7fffffffLL ? 0x7fffffffu : (uint32_t)b;
 }
 
 template <typename T>

@@ -32,9 +32,7 @@ namespace sdpa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per K/V tile
+constexpr int kBN = 64;  // keys per K/V tile
 
 // Maps a linear workgroup id to (query block, b, head). Query blocks are
 // issued from the last (longest under the causal mask) to the first. When
@@ -53,17 +51,27 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
   hq = slot - bi * h_q;
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
+// NW waves per workgroup, 32 query rows per wave.
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
   typedef typename T::elem E;
   typedef typename T::vec8 V8;
+  constexpr int NT = 64 * NW;    // threads
+  constexpr int BM = 32 * NW;    // query rows per workgroup
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
   constexpr int VSTR = kBN + 4;  // LDS row stride (elements) of the transposed V tile
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
   constexpr int NSB = kBN / 32;  // 32-key score blocks per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  constexpr int CH = D / 8;                    // 16-byte chunks per K row
+  constexpr int KCH = kBN * CH / NT;           // K chunks staged per thread
+  constexpr int DG = D / 4;                    // 4-wide column groups of V
+  constexpr int VBL = (kBN / 4) * DG / NT;     // 4x4 V blocks staged per thread
+  static_assert(KCH * NT == kBN * CH && VBL * NT == (kBN / 4) * DG && VBL >= 1, "tile / thread mismatch");
+  // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is written
+  // into the other one; loads for tile t+2 are in flight in registers meanwhile.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -71,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk)
   int qb, bi, hq;
   map_block(blockIdx.x, n_qblk, a.b * a.h_q, a.h_q, qb, bi, hq);
   const int g = hq / (a.h_q / a.h_kv);
-  const int qblk0 = qb * kBM;
+  const int qblk0 = qb * BM;
   const int q0 = qblk0 + wave * 32;
   const int my_q = q0 + j;
 
@@ -97,39 +105,72 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk)
   float l_run = 0.f;        // running sum (this lane half's keys only)
   const float sl2 = a.scale * kLog2e;
 
-  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + kBM) : a.s_kv;
+  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + BM) : a.s_kv;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+  // Staging map. K: thread owns 16-byte chunks (row r, chunk cc). V: thread
+  // owns 4x4 blocks (key group kg, column group dg); each 16-lane group covers
+  // 4 column groups x 4 key groups so that the transposed LDS writes of a
+  // group fall in distinct banks, and each row segment read from HBM is 128 B.
+  // Byte offsets inside a tile are loop-invariant; tiles move the buffer base.
+  uint32_t koff[KCH], kdst[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / CH, cc = c % CH;
+    koff[i] = (uint32_t)(r * a.ks.s * 2 + cc * 16);
+    kdst[i] = r * KSTR + cc * 8;
+  }
+  uint32_t voff[VBL][4], vdst[VBL];
+#pragma unroll
+  for (int i = 0; i < VBL; ++i) {
+    const int c = tid + NT * i;
+    const int sub = c & 15, grp = c >> 4;
+    const int dg = (sub & 3) + 4 * (grp % (DG / 4));
+    const int kg = (sub >> 2) + 4 * (grp / (DG / 4));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) voff[i][r] = (uint32_t)((4 * kg + r) * a.vs.s * 2 + 8 * dg);
+    vdst[i] = (4 * dg) * VSTR + 4 * kg;
+  }
+  u32x4 kreg[KCH];
+  u32x2 vreg[VBL][4];
+  auto load_tile = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, a.s_kv, a.ks.s, D, 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, a.s_kv, a.vs.s, D, 2));
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
+#pragma unroll
+    for (int i = 0; i < VBL; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vreg[i][r] = buf_load8(vr, voff[i][r]);
+  };
+  // Registers -> LDS buffer: K row-major, V transposed (4x4 register transposes).
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Ks[buf][kdst[i]]) = kreg[i];
+#pragma unroll
+    for (int i = 0; i < VBL; ++i) {
+      u32x2 cols[4];
+      transpose4x4_b16(vreg[i], cols);
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&Vt[buf][vdst[i] + c2 * VSTR]) = cols[c2];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(kBN);
+  }
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int k0 = tile * kBN;
-    __syncthreads();
-    // Stage K rows (16-byte chunks) and V (4x4 blocks, stored transposed).
-    {
-      constexpr int CH = D / 8;
-#pragma unroll
-      for (int c = tid; c < kBN * CH; c += 256) {
-        const int r = c / CH, cc = c - (c / CH) * CH;
-        u32x4 val = u32x4{0, 0, 0, 0};
-        if (k0 + r < a.s_kv) val = *(const u32x4*)(kp + (int64_t)(k0 + r) * a.ks.s + cc * 8);
-        *(u32x4*)(&Ks[r * KSTR + cc * 8]) = val;
-      }
-      constexpr int DG = D / 4;
-#pragma unroll
-      for (int c = tid; c < (kBN / 4) * DG; c += 256) {
-        const int dg = c % DG, kg = c / DG;
-        u32x2 rows[4], cols[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 4 * kg + r;
-          rows[r] = u32x2{0, 0};
-          if (key < a.s_kv) rows[r] = *(const u32x2*)(vp + (int64_t)key * a.vs.s + 4 * dg);
-        }
-        transpose4x4_b16(rows, cols);
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&Vt[(4 * dg + c2) * VSTR + 4 * kg]) = cols[c2];
-      }
+    const int buf = tile & 1;
+    __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
+    if (tile + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
     }
-    __syncthreads();
     if (CAUSAL && k0 > q0 + 31) continue;  // every key of this tile is above this wave's rows
 
     // S^T = K Q^T for the 64 keys of the tile.
@@ -139,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk)
       sacc[nb] = f32x16{};
 #pragma unroll
       for (int t = 0; t < NKS; ++t) {
-        const V8 kf = *(const V8*)(&Ks[(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
+        const V8 kf = *(const V8*)(&Ks[buf][(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
         sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
       }
     }
@@ -154,35 +195,40 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk)
           if (key >= a.s_kv || (CAUSAL && key > my_q)) sacc[nb][r] = -INFINITY;
         }
     }
-    // Online softmax: new running max, rescale of the old state.
+    // Online softmax. The running max is only moved (and O, l rescaled) when
+    // some row's max grew by more than 8 (log2 units): with a stale max the
+    // weights stay below 2^8, and the final O / l and LSE are unchanged.
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-    mx = wave_max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    mx = wave_max_halves(mx) * sl2;
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i)
+      for (int i = 0; i < NDB; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
 
     // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand.
     uint32_t pk[NSB][8];
-    float lsum = 0.f;
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -m_new));
-        lsum += p0 + p1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -m_run));
+        lsum0 += p0;
+        lsum1 += p1;
         pk[nb][r / 2] = pack2<T>(p0, p1);
       }
-    l_run += lsum;
+    l_run += lsum0 + lsum1;
 
     // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
@@ -192,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a, int n_qblk)
       const V8 pb = __builtin_bit_cast(V8, bw);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vrow = &Vt[(db * 32 + j) * VSTR + 16 * t2 + 4 * h];
+        const uint16_t* vrow = &Vt[buf][(db * 32 + j) * VSTR + 16 * t2 + 4 * h];
         const u32x2 lo = *(const u32x2*)(vrow);
         const u32x2 hi = *(const u32x2*)(vrow + 8);
         const V8 va = __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
@@ -301,14 +347,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
-  const int n_qblk = (a.s_q + kBM - 1) / kBM;
-  const dim3 grid(n_qblk * a.b * a.h_q), block(256);
+  const int bm = 32 * NW;
+  const int n_qblk = (a.s_q + bm - 1) / bm;
+  const dim3 grid(n_qblk * a.b * a.h_q), block(64 * NW);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW>), grid, block, 0, stream, a, n_qblk);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW>), grid, block, 0, stream, a, n_qblk);
   return hipGetLastError();
 }
 
@@ -325,9 +372,15 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef SDPA_FWD_WAVES
+#define SDPA_FWD_WAVES 8
+#endif
+
 hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream) {
-  if (io == Io::BF16) return a.d == 64 ? launch_mfma_d<Bf16T, 64>(a, stream) : launch_mfma_d<Bf16T, 128>(a, stream);
-  return a.d == 64 ? launch_mfma_d<F16T, 64>(a, stream) : launch_mfma_d<F16T, 128>(a, stream);
+  constexpr int NW = SDPA_FWD_WAVES;
+  if (io == Io::BF16)
+    return a.d == 64 ? launch_mfma_d<Bf16T, 64, 4>(a, stream) : launch_mfma_d<Bf16T, 128, NW>(a, stream);
+  return a.d == 64 ? launch_mfma_d<F16T, 64, 4>(a, stream) : launch_mfma_d<F16T, 128, NW>(a, stream);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
