@@ -76,7 +76,8 @@ typedef enum {
  * recipe). A real input value is x = e4m3(code) * descale_x. Inside the kernel
  * the softmax weights P (all in [0, 1]) are quantised as e4m3(P * scale_p)
  * before the second matmul and the result is multiplied back by descale_p.
- * The usual choice is scale_p = 448, descale_p = 1/448.
+ * The usual choice is scale_p = 448, descale_p = 1/448; scale_p must be <= 448
+ * (SDPA_ERR_INVALID_ARGUMENT otherwise).
  */
 typedef struct {
   float descale_q;

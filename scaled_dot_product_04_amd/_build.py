@@ -10,12 +10,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
-SOURCES = ["sdpa_api.hip", "fwd_kernels.hip", "bwd_kernels.hip"]
+SOURCES = ["sdpa_api.hip", "fwd_kernels.hip", "bwd_kernels.hip", "fp8_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 instructions are disabled for all device code.
+# Packed fp32 instructions are disabled for all device code. MFMA accumulators
+# are kept in arch VGPRs (the kernels size their tiles to fit 256 of them);
+# the default heuristic parks them in AGPRs and copies them every iteration.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(os.path.dirname(PKG), "include")]
 
 

@@ -35,7 +35,7 @@ namespace {
 constexpr int kKvBlock = 128;  // keys per dK/dV workgroup (4 waves x 32)
 constexpr int kQTile = 32;     // query rows per dK/dV inner step
 constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
-constexpr int kKTile = 64;     // keys per dQ inner step
+constexpr int kKTile = 32;     // keys per dQ inner step
 
 // D_i = sum_d dO_id * O_id (fp32); a group of d/8 lanes per row, 16-byte loads.
 template <typename T, int D>
@@ -207,6 +207,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TS];
   __shared__ __attribute__((aligned(16))) float lse2s[2][kQTile];
   __shared__ __attribute__((aligned(16))) float dels[2][kQTile];
+  __shared__ __attribute__((aligned(16))) uint16_t Kb[kKvBlock * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[kKvBlock * RS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -230,16 +232,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const uint16_t* vp = (const uint16_t*)a.v + bi * a.vs.b + g * a.vs.h;
 
   // K and V rows of this lane's key, as B operands (K^T, V^T) of S and dP.
-  V8 kf[NKS], vf[NKS];
-#pragma unroll
-  for (int t = 0; t < NKS; ++t) {
-    if (my_key < a.s_kv) {
-      kf[t] = *(const V8*)(kp + (int64_t)my_key * a.ks.s + 16 * t + 8 * h);
-      vf[t] = *(const V8*)(vp + (int64_t)my_key * a.vs.s + 16 * t + 8 * h);
-    } else {
-      kf[t] = V8{};
-      vf[t] = V8{};
-    }
+  // The workgroup's K and V rows stay in LDS for the whole kernel (staged once,
+  // row-major); each step reads this wave's rows as the B operands of S and dP.
+  // Keeping them in registers instead would exceed the VGPR budget and make
+  // the compiler move accumulators between register files every step.
+  {
+    ChunkTile<kKvBlock, D> kv;
+    kv.init(a.ks.s, tid);
+    kv.load(kp, kb * kKvBlock, a.s_kv, tid);
+    kv.store(Kb, tid);
+    kv.init(a.vs.s, tid);
+    kv.load(vp, kb * kKvBlock, a.s_kv, tid);
+    kv.store(Vb, tid);
   }
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -296,19 +300,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       store_tile(buf ^ 1);
       if (it + 2 < n_it) load_tile(it + 2);
     }
-    if (CAUSAL && q0 + kQTile - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    // (Tiles whose queries all precede this wave's keys are not skipped: the
+    // mask zeroes them, and a branch here would make the compiler copy the
+    // dK/dV accumulators between register files on every iteration.)
 
     // S = Q K^T and dP = dO V^T for 32 queries x this lane's key.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < NKS; ++t) {
       const V8 qa = *(const V8*)(&Qs[buf][j * RS + 16 * t + 8 * h]);
-      s = T::mfma(qa, kf[t], s);
+      s = T::mfma(qa, *(const V8*)(&Kb[(wave * 32 + j) * RS + 16 * t + 8 * h]), s);
       const V8 da = *(const V8*)(&Ds_[buf][j * RS + 16 * t + 8 * h]);
-      dp = T::mfma(da, vf[t], dp);
+      dp = T::mfma(da, *(const V8*)(&Vb[(wave * 32 + j) * RS + 16 * t + 8 * h]), dp);
     }
     // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
     const bool need_mask = CAUSAL ? (q0 < kw0 + 31 || q0 + kQTile > a.s_q) : (q0 + kQTile > a.s_q);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + acc_row(r, h);
+        if (qi >= a.s_q || (CAUSAL && my_key > qi)) s[r] = -INFINITY;
+      }
+    }
     uint32_t ppk[8], dspk[8];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -318,12 +331,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = s[4 * r4 + e];
-        if (need_mask) {
-          const int qi = q0 + row0 + e;
-          if (qi >= a.s_q || (CAUSAL && my_key > qi)) x = -INFINITY;
-        }
-        const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, -l4[e]));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, -l4[e]));
         pv[e] = p;
         dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
       }
@@ -491,8 +499,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       store_tile(buf ^ 1);
       if (tile + 2 < n_tiles) load_tile((tile + 2) * kKTile);
     }
-    if (CAUSAL && k0 > q0 + 31) continue;
-
+    // (Tiles above this wave's diagonal are masked, not skipped: a branch here
+    // makes the compiler copy the dQ accumulators between register files.)
     f32x16 s[NSB], dp[NSB];
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb) {
@@ -507,23 +515,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       }
     }
     const bool need_mask = (k0 + kKTile > a.s_kv) || (CAUSAL && k0 + kKTile - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + nb * 32 + acc_row(r, h);
+          if (key >= a.s_kv || (CAUSAL && key > my_q)) s[nb][r] = -INFINITY;
+        }
+    }
     uint32_t dspk[NSB][8];
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float x = s[nb][r + e];
-          if (need_mask) {
-            const int key = k0 + nb * 32 + acc_row(r + e, h);
-            if (key >= a.s_kv || (CAUSAL && key > my_q)) x = -INFINITY;
-          }
-          const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, -lse2));
-          ds2[e] = p * (dp[nb][r + e] - dl);
-        }
-        dspk[nb][r / 2] = pack2<T>(ds2[0], ds2[1]);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, -lse2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, -lse2));
+        dspk[nb][r / 2] = pack2<T>(p0 * (dp[nb][r] - dl), p1 * (dp[nb][r + 1] - dl));
       }
     // dQ^T += K^T dS^T
 #pragma unroll

@@ -134,6 +134,8 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
     const float f[5] = {fp8->descale_q, fp8->descale_k, fp8->descale_v, fp8->scale_p, fp8->descale_p};
     for (float x : f)
       if (!(x > 0.f) || !isfinite(x)) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 factors must be finite and > 0");
+    if (fp8->scale_p > 448.f)
+      return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 scale_p must be <= 448 (P <= 1 is quantised as P * scale_p)");
   }
   sdpa::Io io;
   bool ok = false;
@@ -148,7 +150,7 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
     ok = d == 64 || d == 128;
   } else if (in_dtype == SDPA_FP8_E4M3 && out_dtype == SDPA_BF16) {
     io = sdpa::Io::FP8;
-    ok = false;  // fp8 kernel not built yet
+    ok = d == 128 || d == 256;
   }
   if (!ok)
     return fail(SDPA_ERR_NOT_SUPPORTED, "no forward kernel for in=%d out=%d d=%d", (int)in_dtype, (int)out_dtype, d);
@@ -190,6 +192,7 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
   hipError_t e;
   switch (io) {
     case sdpa::Io::F32: e = sdpa::launch_fwd_f32(a, stream); break;
+    case sdpa::Io::FP8: e = sdpa::launch_fwd_fp8(a, stream); break;
     default: e = sdpa::launch_fwd_mfma(a, io, stream); break;
   }
   if (e == hipSuccess && g_timing.n >= 2) e = hipEventRecord(g_timing.ev[1], stream);

@@ -55,6 +55,7 @@ enum class Io { F32, F16, BF16, FP8 };
 // Kernel launchers; each returns hipGetLastError() after enqueueing.
 hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te);
 hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
 

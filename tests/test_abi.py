@@ -73,6 +73,10 @@ def _fwd(**kw):
     (dict(q=FAKE + 2), 2, "16-byte aligned"),
     (dict(ks=(64 * 2 * 128, 128, 2 * 128 + 4, 1)), 2, "multiple of 16 bytes"),
     (dict(tin=sdpa.SDPA_FP8_E4M3), 1, "fp8 scales"),
+    (dict(tin=sdpa.SDPA_FP8_E4M3, fp8=ctypes.pointer(sdpa.Fp8Scales(1, 1, 1, 500, 1 / 500))), 1, "scale_p"),
+    (dict(tin=sdpa.SDPA_FP8_E4M3, fp8=ctypes.pointer(sdpa.Fp8Scales(1, 1, 1, 448, 1 / 448)), d=64,
+          qs=_bshd(2, 4, 64, 64)), 2, "no forward kernel"),
+    (dict(fp8=ctypes.pointer(sdpa.Fp8Scales(1, 1, 1, 448, 1 / 448))), 1, "fp8 scales"),
 ])
 def test_forward_validation_errors(kw, status, needle):
     st, msg = _fwd(**kw)

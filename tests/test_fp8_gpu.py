@@ -1,0 +1,68 @@
+"""GPU parity of the fp8 (e4m3) forward against the float64 oracle.
+
+The oracle receives the dequantised inputs (e4m3 code x per-tensor descale)
+and computes the exact softmax; the kernel quantises P to e4m3 for the second
+matmul, which is what the fp8 tolerance absorbs. Checks: max-abs error beyond
+bf16 output rounding <= 1e-1, relative Frobenius error <= 1e-1 (a max-abs bound
+alone would pass an all-zero output at long sequence lengths, where |O| is
+small), and LSE within 1e-3 relative (it does not involve the quantised P)."""
+import math
+
+import numpy as np
+import pytest
+
+import sdpa_inputs
+from sdpa_inputs import Workload
+from tests.parity import TOL, check_lse, excess_err, f64, gpu_fwd, max_abs, oracle_fwd, rel_fro, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, o, lse, o_ref, lse_ref, rows=None):
+    og = f64(o.cpu())
+    lg = lse.cpu().numpy()
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    err, exc, rf = max_abs(og, o_ref), excess_err(og, o_ref, "bf16"), rel_fro(og, o_ref)
+    say(f"    fp8: max|dO|={err:.3e} beyond-rounding={exc:.3e} relF={rf:.3e} max|O|={np.nanmax(np.abs(o_ref)):.3f}")
+    assert exc <= TOL["fp8"], exc
+    assert rf <= TOL["fp8"], rf
+    check_lse(lg, lse_ref)
+    return rf
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_small(d, causal):
+    w = Workload("fp8_small", 2, 4, 4, 300, 300, d, "fp8", "bf16", causal, 1 / math.sqrt(d), "bshd", 17 + d)
+    say(f"[fp8] {w}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = gpu_fwd(w, g)
+    o_ref, lse_ref = oracle_fwd(w, ins)
+    rf = _check(w, o, lse, o_ref, lse_ref)
+    # e4m3 P carries 3 mantissa bits: the relative error is a few percent, not zero
+    assert rf > 1e-4
+
+
+def test_fp8_gqa_ragged():
+    w = Workload("fp8_gqa", 1, 8, 2, 161, 230, 256, "fp8", "bf16", False, 1 / 16, "bhsd", 3)
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = gpu_fwd(w, g)
+    o_ref, lse_ref = oracle_fwd(w, ins)
+    _check(w, o, lse, o_ref, lse_ref)
+
+
+def test_fp8_hd256_full_size_sampled():
+    """b4 h8 s8192 d256 non-causal (the cuDNN 9 blog's fp8 figure shape): sampled rows."""
+    w = sdpa_inputs.fp8()
+    say(f"[fp8 sampled] {w}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = gpu_fwd(w, g)
+    rng = np.random.default_rng(0)
+    heads = [(0, 0), (w.b - 1, w.h_q - 1), (2, 5)]
+    rows = sorted(set([0, 1, 63, 64, 4095, w.s_q - 1] + [int(x) for x in rng.integers(0, w.s_q, 40)]))
+    o_ref, lse_ref = oracle_fwd(w, ins, heads=heads, rows=np.array(rows))
+    _check(w, o, lse, o_ref, lse_ref, rows=rows)
