@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 
@@ -88,6 +89,30 @@ def cpu_baseline(w, ins, n_heads: int) -> dict:
             "seconds": round(dt, 3)}
 
 
+def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
+    """Extra measurement (not part of `value`): the fp8 e4m3 forward on the
+    head-dim-256 non-causal workload (b4 h8 s8192), TFLOP/s vs the fp8 peak."""
+    w = sdpa_inputs.fp8()
+    ins = sdpa_inputs.make_inputs(w)
+    g = {k: sdpa_inputs.to_device_like(v, "cuda:0") for k, v in ins.items() if isinstance(v, torch.Tensor)}
+    sc = sdpa.Fp8Scales(ins["descale_q"], ins["descale_k"], ins["descale_v"], ins["scale_p"], ins["descale_p"])
+    o = sdpa._like_q(g["q"], torch.bfloat16)
+    lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device="cuda:0")
+    for _ in range(warmup):
+        sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=False, out=o, lse=lse, fp8=sc, stream=stream)
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, sh)
+    for _ in range(steps):
+        sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=False, out=o, lse=lse, fp8=sc, stream=stream)
+    hip.record(b, sh)
+    torch.cuda.synchronize()
+    ms = hip.ms(a, b) / steps
+    tf = w.fwd_flops / (ms / 1e3) / 1e12
+    return {"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+            "pct_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +120,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this library has no "
@@ -178,6 +204,11 @@ def main() -> int:
     log(f"[bench] fwd {fwd_tflops:.1f} TFLOP/s ({100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% peak); "
         f"bwd {bwd_tflops:.1f}; fwd+bwd {value:.1f} ({100 * value / PEAK_BF16_TFLOPS:.1f}%)")
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
+        log(f"[bench] fp8 forward (b4 h8 s8192 d256, non-causal): {fp8}")
+
     cpu = None
     if args.cpu_heads > 0:
         cpu = cpu_baseline(w, ins, args.cpu_heads)
@@ -207,6 +238,7 @@ def main() -> int:
         "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
+        "fp8_forward": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
