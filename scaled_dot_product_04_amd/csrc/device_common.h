@@ -78,6 +78,24 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// Row-major LDS tiles read both as MFMA row operands (ds_read_b128 of one
+// row by 8 consecutive lanes) and transposed (ds_read_b64_tr_b16 of 4
+// consecutive rows x 32 bytes by a 16-lane group) store 16-byte chunk c of row
+// r at chunk position c ^ swz(r), with no row padding. With rows a multiple of
+// 128 bytes, both access patterns then touch distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte pieces addressed by lanes 4 j + i / 4 of the group,
+// j = 0..3 (one 16-bit value per j).
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Bytes of rows [row0, n_rows) of a row-major tile with `row_stride` elements
 // between rows and `row_len` elements per row (0 if none), clamped to 2^31.
 __device__ __forceinline__ uint32_t tile_bytes(int row0, int n_rows, int64_t row_stride, int row_len,

@@ -15,7 +15,7 @@
 
 #include <string>
 
-#include "../../include/sdpa.h"
+#include "sdpa.h"
 #include "sdpa_internal.h"
 
 namespace {
