@@ -89,6 +89,32 @@ def cpu_baseline(w, ins, n_heads: int) -> dict:
             "seconds": round(dt, 3)}
 
 
+TRAFFIC_RECORDS = {"bwd_dkdv": "profiles/hd128_causal_s8192_dkdv_hbm_traffic.json"}
+
+
+def sources_digest(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE, scaled by a known-size copy), or None when there
+    is no record or the kernel's sources changed since the counters were taken."""
+    import json
+    rec_path = TRAFFIC_RECORDS.get(kernel)
+    if rec_path is None or not os.path.exists(os.path.join(ROOT, rec_path)):
+        return None
+    rec = json.load(open(os.path.join(ROOT, rec_path)))
+    if sources_digest(rec["sources"]) != rec["sources_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
     """Extra measurement (not part of `value`): the fp8 e4m3 forward on the
     head-dim-256 non-causal workload (b4 h8 s8192), TFLOP/s vs the fp8 peak."""
@@ -121,6 +147,9 @@ def main() -> int:
     ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this library has no "
@@ -131,6 +160,15 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_reference:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB five times")
+        return 0
 
     import scaled_dot_product_04_amd as sdpa
     import sdpa_inputs
@@ -198,7 +236,7 @@ def main() -> int:
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda k: mean[k])
     achieved = kernel_flops[dom] / (mean[dom] / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "kernel_ms_mean": round(mean[dom], 4)}
     log(f"[bench] per-kernel median ms: " + ", ".join(f"{k}={v:.3f}" for k, v in med.items()))
     log(f"[bench] fwd {fwd_tflops:.1f} TFLOP/s ({100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% peak); "
