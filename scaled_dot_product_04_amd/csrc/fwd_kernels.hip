@@ -32,7 +32,6 @@ namespace sdpa {
 
 namespace {
 
-constexpr int kBN = 64;  // keys per K/V tile
 
 // Maps a linear workgroup id to (query block, b, head). Query blocks are
 // issued from the last (longest under the causal mask) to the first. When
@@ -51,31 +50,38 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
   hq = slot - bi * h_q;
 }
 
-#ifndef SDPA_FWD_VTR
-#define SDPA_FWD_VTR 1
-#endif
-#ifndef SDPA_FWD_PP
-#define SDPA_FWD_PP 0
-#endif
+
+// Chunk swizzle of the row-major V tile: row r keeps its 16-byte chunk c at
+// position c ^ vswz<D>(r). The LDS serves a 64-lane 8-byte read in two passes
+// of 32 lanes over 64 banks (256 bytes); in one transposed read, the 32 lanes
+// of a pass touch 4 consecutive rows x 2 column groups of 32 bytes each, and
+// this XOR spreads them over all 16 chunk positions (D = 128: one row per 256
+// bytes, rows 4k..4k+3 shifted by 0, 4, 8, 12 chunks; D = 64: two rows per 256
+// bytes, row pairs shifted by 0 and 4). A pass of 16-byte row stores covers
+// whole rows, which any XOR keeps conflict-free.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2;
+}
 
 // Lane offsets for transposed operand reads from a swizzled row-major tile of
 // D columns (rows = keys): lane (column 32 db + l % 32, half h) receives rows
 // 16 t + 4 h + 0..3 and 16 t + 8 + 4 h + 0..3 via two ds_read_b64_tr_b16.
 template <int D>
 struct SwzLaneF {
-  int tr_off[2];
+  int tr_off[D / 32];
   __device__ __forceinline__ void init(int lane) {
     const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
     const int row = 4 * h + (i >> 2);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int col = 32 * p + 16 * (grp & 1) + 4 * (i & 3);
-      tr_off[p] = row * D + (((col >> 3) ^ swz(row)) * 8) + 4 * ((col >> 2) & 1);
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * (grp & 1) + 4 * (i & 3);
+      tr_off[db] = row * D + (((col >> 3) ^ vswz<D>(row)) * 8) + 4 * ((col >> 2) & 1);
     }
   }
   template <typename V8>
   __device__ __forceinline__ V8 tr(const uint16_t* tile, int db, int t) const {
-    const uint16_t* p = &tile[tr_off[db & 1] + 64 * (db >> 1) + 16 * t * D];
+    const uint16_t* p = &tile[tr_off[db] + 16 * t * D];
     const u32x2 lo = ds_read_tr16(p);
     const u32x2 hi = ds_read_tr16(p + 8 * D);
     return __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
@@ -89,29 +95,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   typedef typename T::vec8 V8;
   constexpr int NT = 64 * NW;    // threads
   constexpr int BM = 32 * NW;    // query rows per workgroup
+  // Keys per K/V tile: 128 at d = 128 (halves the per-tile barrier, row-max
+  // reduction and loop overhead; 244 VGPRs, 135 KB LDS at 8 waves), 64 at
+  // d = 64 (keeps three waves per SIMD).
+  constexpr int kBN = D == 128 ? 128 : 64;
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
-  constexpr int VSTR = kBN + 4;  // LDS row stride (elements) of the transposed V tile
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
   constexpr int NSB = kBN / 32;  // 32-key score blocks per tile
-  constexpr int CH = D / 8;                    // 16-byte chunks per K row
-  constexpr int KCH = kBN * CH / NT;           // K chunks staged per thread
-  constexpr int DG = D / 4;                    // 4-wide column groups of V
-  constexpr int VBL = (kBN / 4) * DG / NT;     // 4x4 V blocks staged per thread
-  static_assert(KCH * NT == kBN * CH && VBL * NT == (kBN / 4) * DG && VBL >= 1, "tile / thread mismatch");
+  constexpr int CH = D / 8;                    // 16-byte chunks per K or V row
+  constexpr int KCH = kBN * CH / NT;           // K (and V) chunks staged per thread
+  static_assert(KCH * NT == kBN * CH, "tile / thread mismatch");
   // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is written
   // into the other one; loads for tile t+2 are in flight in registers meanwhile.
-#if SDPA_FWD_PP
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[3][kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[3][kBN * D];
-#elif SDPA_FWD_VTR
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KSTR];
   // V tile row-major (swizzled 16-byte chunks); V^T operands via transposed reads.
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
-#else
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
-#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -148,11 +147,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + BM) : a.s_kv;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-  // Staging map. K: thread owns 16-byte chunks (row r, chunk cc). V: thread
-  // owns 4x4 blocks (key group kg, column group dg); each 16-lane group covers
-  // 4 column groups x 4 key groups so that the transposed LDS writes of a
-  // group fall in distinct banks, and each row segment read from HBM is 128 B.
-  // Byte offsets inside a tile are loop-invariant; tiles move the buffer base.
+  // Staging map: thread owns 16-byte chunks (row r, chunk cc) of K and of V;
+  // consecutive threads read consecutive chunks of a row from HBM. K rows are
+  // padded in LDS, V rows are swizzled. Byte offsets inside a tile are
+  // loop-invariant; tiles move the buffer base.
   uint32_t koff[KCH], kdst[KCH];
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
@@ -161,166 +159,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     koff[i] = (uint32_t)(r * a.ks.s * 2 + cc * 16);
     kdst[i] = r * KSTR + cc * 8;
   }
-#if SDPA_FWD_VTR
   uint32_t voff2[KCH], vdst2[KCH];
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
     const int c = tid + NT * i;
     const int r = c / CH, cc = c % CH;
     voff2[i] = (uint32_t)(r * a.vs.s * 2 + cc * 16);
-    vdst2[i] = r * D + ((cc ^ swz(r)) * 8);
+    vdst2[i] = r * D + ((cc ^ vswz<D>(r)) * 8);
   }
   u32x4 vreg2[KCH];
   SwzLaneF<D> sl;
   sl.init(lane);
-#endif
-  uint32_t voff[VBL][4], vdst[VBL];
-#pragma unroll
-  for (int i = 0; i < VBL; ++i) {
-    const int c = tid + NT * i;
-    const int sub = c & 15, grp = c >> 4;
-    const int dg = (sub & 3) + 4 * (grp % (DG / 4));
-    const int kg = (sub >> 2) + 4 * (grp / (DG / 4));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) voff[i][r] = (uint32_t)((4 * kg + r) * a.vs.s * 2 + 8 * dg);
-    vdst[i] = (4 * dg) * VSTR + 4 * kg;
-  }
   u32x4 kreg[KCH];
-  u32x2 vreg[VBL][4];
   auto load_tile = [&](int k0) {
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, a.s_kv, a.ks.s, D, 2));
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, a.s_kv, a.vs.s, D, 2));
 #pragma unroll
     for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
-#if SDPA_FWD_VTR
 #pragma unroll
     for (int i = 0; i < KCH; ++i) vreg2[i] = buf_load16(vr, voff2[i]);
-#else
-#pragma unroll
-    for (int i = 0; i < VBL; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[i][r] = buf_load8(vr, voff[i][r]);
-#endif
   };
-  // Registers -> LDS buffer: K row-major, V transposed (4x4 register transposes).
+  // Registers -> LDS buffer.
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) *(u32x4*)(&Ks[buf][kdst[i]]) = kreg[i];
-#if SDPA_FWD_VTR
 #pragma unroll
     for (int i = 0; i < KCH; ++i) *(u32x4*)(&Vs[buf][vdst2[i]]) = vreg2[i];
-#else
-#pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      u32x2 cols[4];
-      transpose4x4_b16(vreg[i], cols);
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&Vt[buf][vdst[i] + c2 * VSTR]) = cols[c2];
-    }
-#endif
   };
 
-#if SDPA_FWD_PP
-  // Two wave groups in a fixed phase offset. The two waves that share a SIMD
-  // (w and w + 4) sit in different groups: in each tile step the leading group
-  // runs S, softmax, P V of tile t while the lagging group runs softmax and
-  // P V of tile t-1 and then S of tile t, so one wave of the pair issues
-  // matrix instructions while the other exponentiates. The per-tile barrier
-  // keeps the offset. Three K/V buffers: in step t, tile t and tile t-1 are
-  // read while tile t+1 is written.
-  auto s_phase = [&](int tile, f32x16 (&sacc)[NSB]) {
-    const int k0 = tile * kBN;
-    const int buf = tile % 3;
-#pragma unroll
-    for (int nb = 0; nb < NSB; ++nb) {
-      sacc[nb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        const V8 kf = *(const V8*)(&Ks[buf][(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
-        sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
-      }
-    }
-    if ((k0 + kBN > a.s_kv) || (CAUSAL && k0 + kBN - 1 > q0)) {
-#pragma unroll
-      for (int nb = 0; nb < NSB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= a.s_kv || (CAUSAL && key > my_q)) sacc[nb][r] = -INFINITY;
-        }
-    }
-  };
-  auto softmax_pv = [&](int tile, const f32x16 (&sacc)[NSB]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < NSB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-    mx = wave_max_halves(mx) * sl2;
-    if (__any(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-    uint32_t pk[NSB][8];
-    float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < NSB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -m_run));
-        lsum0 += p0;
-        lsum1 += p1;
-        pk[nb][r / 2] = pack2<T>(p0, p1);
-      }
-    l_run += lsum0 + lsum1;
-    const uint16_t* vt = Vs[tile % 3];
-#pragma unroll
-    for (int t2 = 0; t2 < kBN / 16; ++t2) {
-      const int nb = t2 / 2, base = 4 * (t2 % 2);
-      const V8 pb = __builtin_bit_cast(V8, u32x4{pk[nb][base], pk[nb][base + 1], pk[nb][base + 2], pk[nb][base + 3]});
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = T::mfma(sl.template tr<V8>(vt, db, t2), pb, oacc[db]);
-    }
-  };
-  auto stage = [&](int tile) {
-    if (tile + 1 < n_tiles) {
-      store_tile((tile + 1) % 3);
-      if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
-    }
-  };
-  auto active = [&](int tile) { return !(CAUSAL && tile * kBN > q0 + 31); };
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(kBN);
-  }
-  const bool lag = NW == 8 && __builtin_amdgcn_readfirstlane(wave) >= 4;
-  f32x16 sacc[NSB];
-  if (!lag) {
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      __syncthreads();
-      stage(tile);
-      if (!active(tile)) continue;
-      s_phase(tile, sacc);
-      softmax_pv(tile, sacc);
-    }
-  } else {
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      __syncthreads();
-      stage(tile);
-      if (tile > 0 && active(tile - 1)) softmax_pv(tile - 1, sacc);
-      if (active(tile)) s_phase(tile, sacc);
-    }
-    if (n_tiles > 0 && active(n_tiles - 1)) softmax_pv(n_tiles - 1, sacc);
-  }
-#else
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -402,20 +268,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
       const V8 pb = __builtin_bit_cast(V8, bw);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-#if SDPA_FWD_VTR
         const V8 va = sl.template tr<V8>(Vs[buf], db, t2);
-#else
-        const uint16_t* vrow = &Vt[buf][(db * 32 + j) * VSTR + 16 * t2 + 4 * h];
-        const u32x2 lo = *(const u32x2*)(vrow);
-        const u32x2 hi = *(const u32x2*)(vrow + 8);
-        const V8 va = __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
-#endif
         oacc[db] = T::mfma(va, pb, oacc[db]);
       }
     }
   }
-
-#endif
 
   // Epilogue: O = O_acc / l, LSE = ln l + m.
   const float l_tot = wave_sum_halves(l_run);
