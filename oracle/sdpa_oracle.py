@@ -28,8 +28,16 @@ design notes of the repository):
 
 * ``stats`` is the natural-log logsumexp of the scaled, masked scores of each
   query row: LSE_i = m_i + ln(sum_j exp(S_ij - m_i)), m_i = max_j S_ij.
-* the causal mask is top-left aligned: key j is visible to query i iff j <= i,
-  also when s_q != s_kv.
+* the causal mask is top-left aligned by default: key j is visible to query i
+  iff j <= i, also when s_q != s_kv. Bottom-right alignment (the option the
+  cuDNN 9 blog's SDPA node call lists next to the padding mask) shifts the
+  diagonal to the end of the key range: j <= i + (s_kv - s_q).
+* the padding mask (the node's ``use_padding_mask`` with per-batch
+  ``seq_len_q`` / ``seq_len_kv``): batch element b uses only its first
+  seq_len_q[b] query rows and first seq_len_kv[b] keys; the bottom-right
+  offset uses those lengths. A query row that sees no key (a padded row, or a
+  row above a bottom-right diagonal) has O = 0 and LSE = -inf and takes no
+  part in the backward (its dQ is 0 and it adds nothing to dK, dV).
 * the backward is the exact gradient of the forward (the pages only show that
   a forward+backward exists), with D_i = sum_d dO_id * O_id.
 * fp8 inputs are the e4m3 codes times a per-tensor fp32 descale; the oracle
@@ -57,26 +65,54 @@ def _kv_head(hq: int, h_q: int, h_kv: int) -> int:
     return hq // (h_q // h_kv)
 
 
-def _masked_scores(q_rows: np.ndarray, row_idx: np.ndarray, kh: np.ndarray,
-                   scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T for the given query rows, with masked entries set to -inf."""
+def _lengths(bi: int, s_q: int, s_kv: int, causal: bool, align: str, seq_len_q, seq_len_kv):
+    """(valid query rows, valid keys, diagonal offset) of batch element bi.
+
+    Key j is visible to query row i < lq iff j < lk and, under the causal mask,
+    j <= i + off, with off = 0 (top-left) or lk - lq (bottom-right).
+    """
+    if align not in ("top_left", "bottom_right"):
+        raise ValueError("align must be 'top_left' or 'bottom_right'")
+    lq = s_q if seq_len_q is None else int(min(max(int(seq_len_q[bi]), 0), s_q))
+    lk = s_kv if seq_len_kv is None else int(min(max(int(seq_len_kv[bi]), 0), s_kv))
+    off = lk - lq if (causal and align == "bottom_right") else 0
+    return lq, lk, off
+
+
+def _masked_scores(q_rows: np.ndarray, row_idx: np.ndarray, kh: np.ndarray, scale: float,
+                   causal: bool, lq: int = None, lk: int = None, off: int = 0) -> np.ndarray:
+    """S = scale * Q K^T for the given query rows, with masked entries set to -inf.
+
+    Masked: keys j >= lk, every key of a row i >= lq, and (causal) j > i + off.
+    """
     s = scale * (q_rows @ kh.T)
+    key_idx = np.arange(kh.shape[0])
+    lq = np.iinfo(np.int64).max if lq is None else lq
+    lk = kh.shape[0] if lk is None else lk
+    vis = (key_idx[None, :] < lk) & (row_idx[:, None] < lq)
     if causal:
-        key_idx = np.arange(kh.shape[0])
-        s = np.where(key_idx[None, :] <= row_idx[:, None], s, -np.inf)
-    return s
+        vis &= key_idx[None, :] <= row_idx[:, None] + off
+    return np.where(vis, s, -np.inf)
 
 
 def _softmax_rows(s: np.ndarray):
-    """Row softmax of S: returns (P, m, l) with P = exp(S - m) / l."""
+    """Row softmax of S: returns (P, m, l) with P = exp(S - m) / l.
+
+    A row whose entries are all -inf (no visible key) gets P = 0, m = -inf and
+    l = 0, so that O = 0 and LSE = m + ln l = -inf.
+    """
     m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
+    empty = ~np.isfinite(m[:, 0])
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe)
     l = e.sum(axis=1, keepdims=True)
-    return e / l, m[:, 0], l[:, 0]
+    p = e / np.where(l > 0, l, 1.0)
+    return p, np.where(empty, -np.inf, m[:, 0]), l[:, 0]
 
 
 def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                      causal: bool, heads=None, rows=None, row_block: int = _ROW_BLOCK):
+                      causal: bool, heads=None, rows=None, row_block: int = _ROW_BLOCK,
+                      seq_len_q=None, seq_len_kv=None, align: str = "top_left"):
     """Forward pass O = softmax(scale * Q K^T + mask) V and LSE, in float64.
 
     Follows the JAX attention codelab's step 1 formula and step 4 dense form
@@ -87,8 +123,12 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d), any real dtype (cast to float64).
     heads: optional list of (b, hq) pairs to compute (default: all).
     rows: optional array of query-row indices to compute (default: all).
+    seq_len_q, seq_len_kv: optional per-batch valid lengths (padding mask),
+    clamped to [0, s_q] and [0, s_kv]; align: "top_left" or "bottom_right"
+    placement of the causal diagonal.
     Returns (O, LSE): O has shape (b, h_q, n_rows, d) and LSE (b, h_q, n_rows);
-    entries for heads not in ``heads`` are NaN.
+    entries for heads not in ``heads`` are NaN. Rows that see no key have
+    O = 0 and LSE = -inf.
     """
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
@@ -99,37 +139,43 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     pairs = [(bi, hi) for bi in range(b) for hi in range(h_q)] if heads is None else heads
     for bi, hq in pairs:
         g = _kv_head(hq, h_q, h_kv)
-        kh = np.asarray(k[bi, g], dtype=np.float64)
-        vh = np.asarray(v[bi, g], dtype=np.float64)
+        lq, lk, off = _lengths(bi, s_q, s_kv, causal, align, seq_len_q, seq_len_kv)
+        kh = np.asarray(k[bi, g, :lk], dtype=np.float64)  # keys past lk are never read
+        vh = np.asarray(v[bi, g, :lk], dtype=np.float64)
         for r0 in range(0, n, row_block):
             ridx = row_idx_all[r0:r0 + row_block]
             qr = np.asarray(q[bi, hq][ridx], dtype=np.float64)
-            s = _masked_scores(qr, ridx, kh, scale, causal)
+            s = _masked_scores(qr, ridx, kh, scale, causal, lq, lk, off)
             p, m, l = _softmax_rows(s)
             out[bi, hq, r0:r0 + len(ridx)] = p @ vh
-            lse[bi, hq, r0:r0 + len(ridx)] = m + np.log(l)
+            with np.errstate(divide="ignore"):  # ln 0 = -inf for rows that see no key
+                lse[bi, hq, r0:r0 + len(ridx)] = m + np.log(l)
     return out, lse
 
 
-def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+                    seq_len_q=None, seq_len_kv=None, align: str = "top_left") -> np.ndarray:
     """The full attention-weight tensor P (b, h_q, s_q, s_kv); small inputs only.
 
-    The "weights" of the JAX attention codelab's step 1 (rows sum to one).
+    The "weights" of the JAX attention codelab's step 1 (rows sum to one; a
+    row that sees no key is all zero).
     """
     b, h_q, s_q, _ = q.shape
-    h_kv = k.shape[1]
-    p_all = np.zeros((b, h_q, s_q, k.shape[2]))
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    p_all = np.zeros((b, h_q, s_q, s_kv))
     for bi in range(b):
+        lq, lk, off = _lengths(bi, s_q, s_kv, causal, align, seq_len_q, seq_len_kv)
         for hq in range(h_q):
-            kh = np.asarray(k[bi, _kv_head(hq, h_q, h_kv)], dtype=np.float64)
+            kh = np.asarray(k[bi, _kv_head(hq, h_q, h_kv), :lk], dtype=np.float64)
             s = _masked_scores(np.asarray(q[bi, hq], dtype=np.float64), np.arange(s_q), kh,
-                               scale, causal)
-            p_all[bi, hq] = _softmax_rows(s)[0]
+                               scale, causal, lq, lk, off)
+            p_all[bi, hq, :, :lk] = _softmax_rows(s)[0]
     return p_all
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
-                       scale: float, causal: bool, kv_heads=None, row_block: int = _ROW_BLOCK):
+                       scale: float, causal: bool, kv_heads=None, row_block: int = _ROW_BLOCK,
+                       seq_len_q=None, seq_len_kv=None, align: str = "top_left"):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for the forward above, in float64.
 
     The pages show only that a forward+backward SDPA exists (the cuDNN 9 blog,
@@ -147,6 +193,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
     dK and dV of a KV head are summed over every query head of its group.
     kv_heads: optional list of (b, g) pairs to compute (default: all); the
     other entries are NaN. dQ is filled for the query heads of those groups.
+    seq_len_q, seq_len_kv, align: as in ``attention_forward``; rows that see
+    no key have P = 0, hence dQ = 0 and no contribution to dK, dV.
     """
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
@@ -156,8 +204,9 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
     dv = np.full((b, h_kv, s_kv, d), np.nan)
     groups = [(bi, g) for bi in range(b) for g in range(h_kv)] if kv_heads is None else kv_heads
     for bi, g in groups:
-        kh = np.asarray(k[bi, g], dtype=np.float64)
-        vh = np.asarray(v[bi, g], dtype=np.float64)
+        lq, lk, off = _lengths(bi, s_q, s_kv, causal, align, seq_len_q, seq_len_kv)
+        kh = np.asarray(k[bi, g, :lk], dtype=np.float64)  # keys past lk are never read
+        vh = np.asarray(v[bi, g, :lk], dtype=np.float64)
         dk_g = np.zeros((s_kv, d))
         dv_g = np.zeros((s_kv, d))
         for hq in range(g * grp, (g + 1) * grp):
@@ -165,17 +214,17 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
             qh = np.asarray(q[bi, hq], dtype=np.float64)
             doh = np.asarray(dout[bi, hq], dtype=np.float64)
             dq_h = np.zeros((s_q, d))
-            for r0 in range(0, s_q, row_block):
-                ridx = np.arange(r0, min(s_q, r0 + row_block))
+            for r0 in range(0, lq, row_block):  # rows past lq are never read; their dQ is 0
+                ridx = np.arange(r0, min(lq, r0 + row_block))
                 qr, dor = qh[ridx], doh[ridx]
-                p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal))
+                p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal, lq, lk, off))
                 o = p @ vh
                 dvec = (dor * o).sum(axis=1)
-                dv_g += p.T @ dor
+                dv_g[:lk] += p.T @ dor
                 dp = dor @ vh.T
                 ds = p * (dp - dvec[:, None])
                 dq_h[ridx] = scale * (ds @ kh)
-                dk_g += scale * (ds.T @ qr)
+                dk_g[:lk] += scale * (ds.T @ qr)
             dq[bi, hq] = dq_h
         dk[bi, g] = dk_g
         dv[bi, g] = dv_g
