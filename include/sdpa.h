@@ -41,8 +41,10 @@
  *  - b == 0 or s_q == 0 is an empty problem: sdpa_fwd enqueues nothing; sdpa_bwd
  *    writes zeros to dK and dV (no query attends to them) and nothing else.
  *  - attn_scale must be finite and > 0 (the pages use 1/sqrt(d)).
- *  - Causal alignment is top-left: query i sees keys 0..i, also when
- *    s_q != s_kv; every query row therefore sees at least key 0.
+ *  - Causal alignment of sdpa_fwd / sdpa_bwd is top-left: query i sees keys
+ *    0..i, also when s_q != s_kv; every query row therefore sees at least
+ *    key 0. sdpa_fwd_ex / sdpa_bwd_ex add bottom-right alignment and the
+ *    padding mask (per-batch valid lengths).
  */
 #ifndef SDPA_H_
 #define SDPA_H_
@@ -79,6 +81,22 @@ typedef enum {
  * The usual choice is scale_p = 448, descale_p = 1/448; scale_p must be <= 448
  * (SDPA_ERR_INVALID_ARGUMENT otherwise).
  */
+/*
+ * Attention mask of sdpa_fwd_ex / sdpa_bwd_ex. The cuDNN 9 blog's SDPA node
+ * call ("SDPA usage") lists the causal flag next to use_padding_mask with
+ * per-batch seq_len_q / seq_len_kv; where the causal diagonal sits when the
+ * query and key ranges differ is not on the pages, so both placements exist:
+ *   SDPA_MASK_CAUSAL               top-left: key j visible to row i iff j <= i
+ *   SDPA_MASK_CAUSAL_BOTTOM_RIGHT  key j visible to row i iff j <= i + (lk - lq),
+ *                                  lq / lk the batch element's valid lengths
+ *                                  (the last valid row sees every valid key)
+ */
+typedef enum {
+  SDPA_MASK_NONE = 0,
+  SDPA_MASK_CAUSAL = 1,
+  SDPA_MASK_CAUSAL_BOTTOM_RIGHT = 2
+} sdpa_mask_t;
+
 typedef struct {
   float descale_q;
   float descale_k;
@@ -112,6 +130,31 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
                        const sdpa_fp8_scales_t* fp8, hipStream_t stream);
 
 /*
+ * Forward with an explicit mask and the padding mask (the cuDNN 9 blog's
+ * SDPA node options use_padding_mask / seq_len_q / seq_len_kv, "SDPA usage").
+ * Same arguments and support matrix as sdpa_fwd, with `causal` replaced by:
+ *   mask        an sdpa_mask_t (SDPA_ERR_INVALID_ARGUMENT otherwise).
+ *   seq_len_q   device int32 [b], 4-byte aligned, or NULL (every batch element
+ *               has s_q rows): batch element i uses only its first
+ *               seq_len_q[i] query rows.
+ *   seq_len_kv  device int32 [b] or NULL (= s_kv): batch element i uses only
+ *               its first seq_len_kv[i] keys; K/V rows past it are never read.
+ * The lengths are read by the kernels (no host synchronisation); values are
+ * clamped to [0, s_q] and [0, s_kv]. A query row that sees no key (a row at or
+ * past seq_len_q[i], or under bottom-right alignment a row above the shifted
+ * diagonal) gets O = 0 and LSE = -inf. sdpa_fwd(..., causal, ...) equals
+ * sdpa_fwd_ex(..., causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, NULL, NULL, ...).
+ */
+sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                          const int64_t q_stride[4], const int64_t k_stride[4],
+                          const int64_t v_stride[4], const int64_t o_stride[4],
+                          float attn_scale, sdpa_mask_t mask,
+                          const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                          sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
+                          const sdpa_fp8_scales_t* fp8, hipStream_t stream);
+
+/*
  * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned
  * use). 0 is a valid answer only for empty problems.
  */
@@ -141,6 +184,28 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
                        const int64_t dk_stride[4], const int64_t dv_stride[4],
                        float attn_scale, int causal, sdpa_dtype_t dtype,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward with an explicit mask and the padding mask; the arguments of
+ * sdpa_bwd with `causal` replaced by mask / seq_len_q / seq_len_kv, which must
+ * be those of the forward that produced o and lse (same meaning and clamping as
+ * in sdpa_fwd_ex). Rows that see no key (LSE = -inf) take no part: their dQ is
+ * 0 and they add nothing to dK, dV; keys at or past seq_len_kv[i] get
+ * dK = dV = 0; dQ rows at or past seq_len_q[i] are 0. The workspace size is
+ * that of sdpa_bwd_workspace_size for the same shape.
+ */
+sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse,
+                          void* dq, void* dk, void* dv,
+                          int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                          const int64_t q_stride[4], const int64_t k_stride[4],
+                          const int64_t v_stride[4], const int64_t o_stride[4],
+                          const int64_t do_stride[4], const int64_t dq_stride[4],
+                          const int64_t dk_stride[4], const int64_t dv_stride[4],
+                          float attn_scale, sdpa_mask_t mask,
+                          const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                          sdpa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * Timing hook (diagnostics only; GPU-time-only reporting as in the cuDNN 9

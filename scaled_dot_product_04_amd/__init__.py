@@ -20,6 +20,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_FP8_E4M3 = 0, 1, 2, 3
+SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_INVALID_ARGUMENT", 2: "SDPA_ERR_NOT_SUPPORTED",
                 3: "SDPA_ERR_WORKSPACE_TOO_SMALL", 4: "SDPA_ERR_HIP"}
 
@@ -64,12 +65,19 @@ def load_library() -> ctypes.CDLL:
     lib.sdpa_fwd.restype = ctypes.c_int
     lib.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, i, i,
                              ctypes.POINTER(Fp8Scales), vp]
+    lib.sdpa_fwd_ex.restype = ctypes.c_int
+    lib.sdpa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp, i, i,
+                                ctypes.POINTER(Fp8Scales), vp]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.sdpa_bwd.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                              i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, i, vp,
                              ctypes.c_size_t, vp]
+    lib.sdpa_bwd_ex.restype = ctypes.c_int
+    lib.sdpa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, vp, vp, i, vp,
+                                ctypes.c_size_t, vp]
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -110,27 +118,60 @@ def _like_q(q: torch.Tensor, dtype) -> torch.Tensor:
     return phys.permute(*inv)
 
 
-def fwd(q, k, v, *, scale: float, causal: bool, out=None, lse=None, return_lse: bool = True,
-        fp8: Fp8Scales | None = None, out_dtype=None, stream=None):
+def _mask_code(causal) -> int:
+    """causal: False / True (top-left) / "top_left" / "bottom_right" -> sdpa_mask_t."""
+    if causal is True or causal == "top_left":
+        return SDPA_MASK_CAUSAL
+    if causal == "bottom_right":
+        return SDPA_MASK_CAUSAL_BOTTOM_RIGHT
+    if causal is False or causal is None:
+        return SDPA_MASK_NONE
+    raise ValueError(f"causal must be a bool, 'top_left' or 'bottom_right', not {causal!r}")
+
+
+def _lens(t, b, device, name):
+    """Check a per-batch length tensor (device int32 [b]) and return its pointer."""
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != b or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape ({b},)")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: bool = True,
+        fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, stream=None):
     """O (and LSE) of fused attention. Returns (out, lse); lse is None in inference mode.
 
     q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d); all on the GPU.
+    causal: False, True / "top_left", or "bottom_right" (diagonal through the
+    last valid query row and key).
     fp8: factors for e4m3 inputs (then out_dtype defaults to bfloat16).
+    seq_len_q, seq_len_kv: optional device int32 [b] valid lengths (padding
+    mask); rows that see no key get O = 0 and LSE = -inf.
     """
     lib = load_library()
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
     in_code = _DTYPE_CODES[q.dtype]
+    mask = _mask_code(causal)
+    lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
     if out_dtype is None:
         out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if out is None:
         out = _like_q(q, out_dtype)
     if lse is None and return_lse:
         lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
-    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
-                      _strides(q), _strides(k), _strides(v), _strides(out), float(scale), int(causal),
-                      in_code, _DTYPE_CODES[out.dtype],
-                      ctypes.byref(fp8) if fp8 is not None else None, _stream(stream))
+    fp8_arg = ctypes.byref(fp8) if fp8 is not None else None
+    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None:
+        st = lib.sdpa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
+                             _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask, lq, lk,
+                             in_code, _DTYPE_CODES[out.dtype], fp8_arg, _stream(stream))
+    else:
+        st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
+                          _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask,
+                          in_code, _DTYPE_CODES[out.dtype], fp8_arg, _stream(stream))
     _check(st)
     return out, lse
 
@@ -140,26 +181,35 @@ def bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, dtype) -> int:
                                                       _DTYPE_CODES[dtype]))
 
 
-def bwd(q, k, v, o, dout, lse, *, scale: float, causal: bool, dq=None, dk=None, dv=None,
-        workspace=None, stream=None):
-    """(dQ, dK, dV) of L = sum(O * dO). dK/dV are summed over each KV head's query group."""
+def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, dv=None,
+        workspace=None, seq_len_q=None, seq_len_kv=None, stream=None):
+    """(dQ, dK, dV) of L = sum(O * dO). dK/dV are summed over each KV head's query group.
+
+    causal, seq_len_q, seq_len_kv: those of the forward that produced o and lse.
+    """
     lib = load_library()
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
+    mask = _mask_code(causal)
+    lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
     dq = _like_q(q, q.dtype) if dq is None else dq
     dk = _like_q(k, k.dtype) if dk is None else dk
     dv = _like_q(v, v.dtype) if dv is None else dv
     if workspace is None:
-        n = bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, q.dtype)
+        n = bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, mask != SDPA_MASK_NONE, q.dtype)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
-    st = lib.sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-                      _ptr(dv), b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v),
-                      _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv),
-                      float(scale), int(causal), _DTYPE_CODES[q.dtype], _ptr(workspace),
-                      workspace.numel(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v), _strides(o),
+            _strides(dout), _strides(dq), _strides(dk), _strides(dv), float(scale))
+    tail = (_DTYPE_CODES[q.dtype], _ptr(workspace), workspace.numel(), _stream(stream))
+    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None:
+        st = lib.sdpa_bwd_ex(*args, mask, lq, lk, *tail)
+    else:
+        st = lib.sdpa_bwd(*args, mask, *tail)
     _check(st)
     return dq, dk, dv
 
 
 __all__ = ["fwd", "bwd", "bwd_workspace_size", "load_library", "library_path", "Fp8Scales",
-           "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3"]
+           "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3", "SDPA_MASK_NONE",
+           "SDPA_MASK_CAUSAL", "SDPA_MASK_CAUSAL_BOTTOM_RIGHT"]

@@ -51,13 +51,16 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
     const int i = (int)(r % a.s_q);
     const int64_t bh = r / a.s_q;
     const int hq = (int)(bh % a.h_q), bi = (int)(bh / a.h_q);
-    const uint16_t* op = (const uint16_t*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)i * a.os.s + part * 8;
-    const uint16_t* dp = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)i * a.dos.s + part * 8;
-    const u32x4 ov = *(const u32x4*)op, dv = *(const u32x4*)dp;
+    const int lq = a.seq_q ? min(max(a.seq_q[bi], 0), a.s_q) : a.s_q;
+    if (i < lq) {  // padded rows keep D = 0; their O and dO are never read
+      const uint16_t* op = (const uint16_t*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)i * a.os.s + part * 8;
+      const uint16_t* dp = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)i * a.dos.s + part * 8;
+      const u32x4 ov = *(const u32x4*)op, dv = *(const u32x4*)dp;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(to_f32<T>((uint16_t)(ov[w] & 0xffff)), to_f32<T>((uint16_t)(dv[w] & 0xffff)), acc);
-      acc = fmaf(to_f32<T>((uint16_t)(ov[w] >> 16)), to_f32<T>((uint16_t)(dv[w] >> 16)), acc);
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(to_f32<T>((uint16_t)(ov[w] & 0xffff)), to_f32<T>((uint16_t)(dv[w] & 0xffff)), acc);
+        acc = fmaf(to_f32<T>((uint16_t)(ov[w] >> 16)), to_f32<T>((uint16_t)(dv[w] >> 16)), acc);
+      }
     }
   }
 #pragma unroll
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const int g = bg % a.h_kv, bi = bg / a.h_kv;
   const int G = a.h_q / a.h_kv, Gs = G / n_split;
   (void)n_kblk;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
 
   const int kw0 = kb * kKvBlock + wave * 32;
   const int my_key = kw0 + j;
@@ -239,10 +243,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   {
     ChunkTile<kKvBlock, D> kv;
     kv.init(a.ks.s, tid);
-    kv.load(kp, kb * kKvBlock, a.s_kv, tid);
+    kv.load(kp, kb * kKvBlock, L.lk, tid);  // keys at or past lk read as zero
     kv.store(Kb, tid);
     kv.init(a.vs.s, tid);
-    kv.load(vp, kb * kKvBlock, a.s_kv, tid);
+    kv.load(vp, kb * kKvBlock, L.lk, tid);
     kv.store(Vb, tid);
   }
   f32x16 dk[NDB], dv[NDB];
@@ -252,9 +256,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     dv[i] = f32x16{};
   }
   const float sl2 = a.scale * kLog2e;
-  const int n_qt = (a.s_q + kQTile - 1) / kQTile;
-  const int qt0 = CAUSAL ? min(n_qt, (kb * kKvBlock) / kQTile) : 0;
-  const int nq = n_qt - qt0;
+  // Query tiles of valid rows that can see a key of this block: row i sees
+  // key j iff j <= i + off, so causal rows start at (block start) - off. A
+  // block made only of keys past lk has no work (its dK, dV are zero).
+  const int n_qt = (L.lq + kQTile - 1) / kQTile;
+  const int qt0 = CAUSAL ? min(n_qt, max(0, kb * kKvBlock - L.off) / kQTile) : 0;
+  const int nq = kb * kKvBlock >= L.lk ? 0 : n_qt - qt0;
   const int n_it = Gs * nq;
   const int hq_base = g * G + sp * Gs;
 
@@ -267,13 +274,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     const int q0 = (qt0 + it % nq) * kQTile;
     const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h;
     const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h;
-    qreg.load(qp, q0, a.s_q, tid);
-    dreg.load(dop, q0, a.s_q, tid);
+    qreg.load(qp, q0, L.lq, tid);  // rows at or past lq read as zero
+    dreg.load(dop, q0, L.lq, tid);
     if (tid < kQTile) {
       const int qi = q0 + tid;
       const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + qi;
-      lreg = qi < a.s_q ? a.lse[row] * kLog2e : 0.f;
-      creg = qi < a.s_q ? a.delta[row] : 0.f;
+      // A row that sees no key has LSE = -inf; all its scores are masked, and
+      // 0 here keeps exp2(-inf - lse) at 0 instead of NaN.
+      const float lse = qi < L.lq ? a.lse[row] : 0.f;
+      lreg = lse == -INFINITY ? 0.f : lse * kLog2e;
+      creg = qi < L.lq ? a.delta[row] : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -314,12 +324,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       dp = T::mfma(da, *(const V8*)(&Vb[(wave * 32 + j) * RS + 16 * t + 8 * h]), dp);
     }
     // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
-    const bool need_mask = CAUSAL ? (q0 < kw0 + 31 || q0 + kQTile > a.s_q) : (q0 + kQTile > a.s_q);
+    const bool need_mask = (q0 + kQTile > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + acc_row(r, h);
-        if (qi >= a.s_q || (CAUSAL && my_key > qi)) s[r] = -INFINITY;
+        if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
       }
     }
     uint32_t ppk[8], dspk[8];
@@ -445,6 +455,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   const int qblk0 = qb * kQBlock;
   const int q0 = qblk0 + wave * 32;
   const int my_q = q0 + j;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
 
   const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h;
   const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h;
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   V8 qf[NKS], df[NKS];
 #pragma unroll
   for (int t = 0; t < NKS; ++t) {
-    if (my_q < a.s_q) {
+    if (my_q < L.lq) {
       qf[t] = *(const V8*)(qp + (int64_t)my_q * a.qs.s + 16 * t + 8 * h);
       df[t] = *(const V8*)(dop + (int64_t)my_q * a.dos.s + 16 * t + 8 * h);
     } else {
@@ -463,23 +474,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
     }
   }
   const int64_t row_bh = ((int64_t)bi * a.h_q + hq) * a.s_q;
-  const float lse2 = my_q < a.s_q ? a.lse[row_bh + my_q] * kLog2e : 0.f;
-  const float dl = my_q < a.s_q ? a.delta[row_bh + my_q] : 0.f;
+  // Rows past lq have Q = dO = 0, so their dS and dQ are 0. A row that sees
+  // no key has LSE = -inf and every score masked: 0 keeps its P at 0.
+  const float lse = my_q < L.lq ? a.lse[row_bh + my_q] : 0.f;
+  const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
+  const float dl = my_q < L.lq ? a.delta[row_bh + my_q] : 0.f;
   const float sl2 = a.scale * kLog2e;
 
   f32x16 dq[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + kQBlock) : a.s_kv;
+  const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + kQBlock, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kKTile - 1) / kKTile;
   KTile kreg;
   VTile vreg;
   kreg.init(a.ks.s, tid);
   vreg.init(a.vs.s, tid);
   auto load_tile = [&](int k0) {
-    kreg.load(kp, k0, a.s_kv, tid);
-    vreg.load(vp, k0, a.s_kv, tid);
+    kreg.load(kp, k0, L.lk, tid);  // keys at or past lk read as zero
+    vreg.load(vp, k0, L.lk, tid);
   };
   auto store_tile = [&](int buf) {
     kreg.store_rm(Ks[buf], tid);
@@ -514,14 +528,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
         dp[nb] = T::mfma(va, df[t], dp[nb]);
       }
     }
-    const bool need_mask = (k0 + kKTile > a.s_kv) || (CAUSAL && k0 + kKTile - 1 > q0);
+    const bool need_mask = (k0 + kKTile > L.lk) || (CAUSAL && k0 + kKTile - 1 > q0 + L.off);
     if (need_mask) {
 #pragma unroll
       for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= a.s_kv || (CAUSAL && key > my_q)) s[nb][r] = -INFINITY;
+          if (key >= L.lk || (CAUSAL && key > my_q + L.off)) s[nb][r] = -INFINITY;
         }
     }
     uint32_t dspk[NSB][8];

@@ -98,6 +98,22 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 
 // Bytes of rows [row0, n_rows) of a row-major tile with `row_stride` elements
 // between rows and `row_len` elements per row (0 if none), clamped to 2^31.
+// Lengths of batch element bi under the padding mask: lq valid query rows,
+// lk valid keys (per-batch device arrays, clamped to [0, s]; null = full), and
+// the causal diagonal offset: key j is visible to row i iff j <= i + off, with
+// off = lk - lq for bottom-right alignment, 0 for top-left. Uniform per block.
+struct BatchLens {
+  int lq, lk, off;
+};
+__device__ __forceinline__ BatchLens batch_lens(const int32_t* seq_q, const int32_t* seq_kv, int bi, int s_q,
+                                                int s_kv, bool causal, int bottom_right) {
+  BatchLens r;
+  r.lq = seq_q ? min(max(__builtin_amdgcn_readfirstlane(seq_q[bi]), 0), s_q) : s_q;
+  r.lk = seq_kv ? min(max(__builtin_amdgcn_readfirstlane(seq_kv[bi]), 0), s_kv) : s_kv;
+  r.off = (causal && bottom_right) ? r.lk - r.lq : 0;
+  return r;
+}
+
 __device__ __forceinline__ uint32_t tile_bytes(int row0, int n_rows, int64_t row_stride, int row_len,
                                                int elem_bytes) {
   if (row0 >= n_rows) return 0u;

@@ -85,6 +85,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   const int qblk0 = qb * kBM8;
   const int q0 = qblk0 + wave * 32;
   const int my_q = q0 + j;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
 
   const uint8_t* qp = (const uint8_t*)a.q + bi * a.qs.b + hq * a.qs.h;
   const uint8_t* kp = (const uint8_t*)a.k + bi * a.ks.b + g * a.ks.h;
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   i32x8 qf[NKS];
 #pragma unroll
   for (int t = 0; t < NKS; ++t) {
-    if (my_q < a.s_q) {
+    if (my_q < L.lq) {
       const u32x4 lo = *(const u32x4*)(qp + (int64_t)my_q * a.qs.s + 64 * t + 32 * h);
       const u32x4 hi = *(const u32x4*)(qp + (int64_t)my_q * a.qs.s + 64 * t + 32 * h + 16);
       qf[t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   const float sl2 = a.scale * kLog2e;
   const float lsp = __log2f(a.scale_p);  // weights are produced pre-multiplied by scale_p
 
-  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + kBM8) : a.s_kv;
+  const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + kBM8, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kBN8 - 1) / kBN8;
 
   // Staging map. K: 16-byte chunks (row r, chunk cc). V: blocks of 4 keys x 16
@@ -139,8 +140,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   u32x4 vreg[VBL][4];
   const uint32_t vrow = (uint32_t)a.vs.s;
   auto load_tile = [&](int k0) {
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, a.s_kv, a.ks.s, D, 1));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, a.s_kv, a.vs.s, D, 1));
+    // Rows at or past lk read as zero (never the caller's padding).
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 1));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 1));
 #pragma unroll
     for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
 #pragma unroll
@@ -194,14 +196,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
         sacc[nb] = mfma_fp8(kf, qf[t], sacc[nb]);
       }
     }
-    const bool need_mask = (k0 + kBN8 > a.s_kv) || (CAUSAL && k0 + kBN8 - 1 > q0);
+    const bool need_mask = (k0 + kBN8 > L.lk) || (CAUSAL && k0 + kBN8 - 1 > q0 + L.off);
     if (need_mask) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= a.s_kv || (CAUSAL && key > my_q)) sacc[nb][r] = -INFINITY;
+          if (key >= L.lk || (CAUSAL && key > my_q + L.off)) sacc[nb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -212,7 +214,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
     mx = wave_max_halves(mx) * sl2;
     if (__any(mx > m_run)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
     // p * scale_p = exp2(S * scale * log2e - m + log2(scale_p)) in fp32: its
     // sum is l * scale_p; its e4m3 rounding is packed as the B operand, byte
     // m = 16 nb + r of this lane half.
-    const float off = lsp - m_run;
+    const float off = lsp - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
     uint32_t pw[8];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -252,7 +255,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   }
 
   const float l_tot = wave_sum_halves(l_run);  // = l * scale_p
-  const float inv = a.descale_v * a.descale_p * a.scale_p / l_tot;
+  // Rows past lq, and rows that see no key: O = 0, LSE = -inf.
+  const bool live = my_q < L.lq && l_tot > 0.f;
+  const float inv = live ? a.descale_v * a.descale_p * a.scale_p / l_tot : 0.f;
   if (my_q < a.s_q) {
     uint16_t* op = (uint16_t*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
         *(u32x2*)(op + d0) = w;
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = (m_run + __log2f(l_tot) - lsp) * kLn2;
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + __log2f(l_tot) - lsp) * kLn2 : -INFINITY;
   }
 }
 

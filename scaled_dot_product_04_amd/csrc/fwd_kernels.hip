@@ -121,6 +121,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   const int qblk0 = qb * BM;
   const int q0 = qblk0 + wave * 32;
   const int my_q = q0 + j;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
 
   const E* qp = (const E*)a.q + bi * a.qs.b + hq * a.qs.h;
   const E* kp = (const E*)a.k + bi * a.ks.b + g * a.ks.h;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   V8 qf[NKS];
 #pragma unroll
   for (int t = 0; t < NKS; ++t) {
-    if (my_q < a.s_q) {
+    if (my_q < L.lq) {
       qf[t] = *(const V8*)(qp + (int64_t)my_q * a.qs.s + 16 * t + 8 * h);
     } else {
       qf[t] = V8{};
@@ -144,7 +145,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   float l_run = 0.f;        // running sum (this lane half's keys only)
   const float sl2 = a.scale * kLog2e;
 
-  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + BM) : a.s_kv;
+  // Keys visible to some row of this block: below lk and, under the causal
+  // mask, at most (last valid row) + off.
+  const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + BM, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   // Staging map: thread owns 16-byte chunks (row r, chunk cc) of K and of V;
@@ -172,8 +175,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   sl.init(lane);
   u32x4 kreg[KCH];
   auto load_tile = [&](int k0) {
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, a.s_kv, a.ks.s, D, 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, a.s_kv, a.vs.s, D, 2));
+    // Rows at or past lk read as zero (never the caller's padding).
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
 #pragma unroll
     for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
 #pragma unroll
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
       store_tile(buf ^ 1);
       if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
     }
-    if (CAUSAL && k0 > q0 + 31) continue;  // every key of this tile is above this wave's rows
+    if (CAUSAL && k0 > q0 + 31 + L.off) continue;  // every key of this tile is above this wave's rows
 
     // S^T = K Q^T for the 64 keys of the tile.
     f32x16 sacc[NSB];
@@ -214,15 +218,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
       }
     }
-    // Causal / ragged-tail mask (only tiles that cross the diagonal or the end).
-    const bool need_mask = (k0 + kBN > a.s_kv) || (CAUSAL && k0 + kBN - 1 > q0);
+    // Causal / key-length mask (only tiles that cross the diagonal or lk).
+    const bool need_mask = (k0 + kBN > L.lk) || (CAUSAL && k0 + kBN - 1 > q0 + L.off);
     if (need_mask) {
 #pragma unroll
       for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= a.s_kv || (CAUSAL && key > my_q)) sacc[nb][r] = -INFINITY;
+          if (key >= L.lk || (CAUSAL && key > my_q + L.off)) sacc[nb][r] = -INFINITY;
         }
     }
     // Online softmax. The running max is only moved (and O, l rescaled) when
@@ -236,7 +240,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     mx = wave_max_halves(mx) * sl2;
     if (__any(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -245,15 +250,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
 
-    // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand.
+    // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand
+    // (m = -inf only while every score of the row is -inf: P = 0).
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
     uint32_t pk[NSB][8];
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -m_run));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -msub));
         lsum0 += p0;
         lsum1 += p1;
         pk[nb][r / 2] = pack2<T>(p0, p1);
@@ -274,9 +281,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     }
   }
 
-  // Epilogue: O = O_acc / l, LSE = ln l + m.
+  // Epilogue: O = O_acc / l, LSE = ln l + m. Rows past lq, and rows that see
+  // no key, get O = 0 and LSE = -inf.
   const float l_tot = wave_sum_halves(l_run);
-  const float inv = 1.f / l_tot;
+  const bool live = my_q < L.lq && l_tot > 0.f;
+  const float inv = live ? 1.f / l_tot : 0.f;
   if (my_q < a.s_q) {
     E* op = (E*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         *(u32x2*)(op + d0) = w;
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -307,6 +316,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   const int g = hq / (a.h_q / a.h_kv);
   const int qblk0 = qb * 64;
   const int my_q = qblk0 + tid;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
   const float* qp = (const float*)a.q + bi * a.qs.b + hq * a.qs.h;
   const float* kp = (const float*)a.k + bi * a.ks.b + g * a.ks.h;
   const float* vp = (const float*)a.v + bi * a.vs.b + g * a.vs.h;
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
 #pragma unroll
   for (int d4 = 0; d4 < D; d4 += 4) {
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (my_q < a.s_q) x = *(const f32x4*)(qp + (int64_t)my_q * a.qs.s + d4);
+    if (my_q < L.lq) x = *(const f32x4*)(qp + (int64_t)my_q * a.qs.s + d4);
     qv[d4] = x[0] * sl2;
     qv[d4 + 1] = x[1] * sl2;
     qv[d4 + 2] = x[2] * sl2;
@@ -324,13 +334,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
     o[d4] = o[d4 + 1] = o[d4 + 2] = o[d4 + 3] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
-  const int kv_end = CAUSAL ? min(a.s_kv, qblk0 + 64) : a.s_kv;
+  const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + 64, L.lq) + L.off)) : L.lk;
   for (int k0 = 0; k0 < kv_end; k0 += BN) {
     __syncthreads();
     for (int c = tid; c < BN * D / 4; c += 64) {
       const int r = c / (D / 4), d4 = 4 * (c % (D / 4));
       f32x4 kx = f32x4{0.f, 0.f, 0.f, 0.f}, vx = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (k0 + r < a.s_kv) {
+      if (k0 + r < L.lk) {
         kx = *(const f32x4*)(kp + (int64_t)(k0 + r) * a.ks.s + d4);
         vx = *(const f32x4*)(vp + (int64_t)(k0 + r) * a.vs.s + d4);
       }
@@ -346,31 +356,36 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) acc = fmaf(qv[dd], Ks[jj * D + dd], acc);
       const int key = k0 + jj;
-      if (key >= a.s_kv || (CAUSAL && key > my_q)) acc = -INFINITY;
+      if (key >= L.lk || (CAUSAL && key > my_q + L.off)) acc = -INFINITY;
       s[jj] = acc;
       mx = fmaxf(mx, acc);
     }
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // m stays -inf while every score of the row is -inf: P = 0, nothing to rescale.
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int dd = 0; dd < D; ++dd) o[dd] *= alpha;
 #pragma unroll
     for (int jj = 0; jj < BN; ++jj) {
-      const float p = __builtin_amdgcn_exp2f(s[jj] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[jj] - msub);
       l_run += p;
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) o[dd] = fmaf(p, Vs[jj * D + dd], o[dd]);
     }
   }
   if (my_q < a.s_q) {
-    const float inv = 1.f / l_run;
+    // Rows past lq, and rows that see no key: O = 0, LSE = -inf.
+    const bool live = my_q < L.lq && l_run > 0.f;
+    const float inv = live ? 1.f / l_run : 0.f;
     float* op = (float*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
     for (int d4 = 0; d4 < D; d4 += 4)
       *(f32x4*)(op + d4) = f32x4{o[d4] * inv, o[d4 + 1] * inv, o[d4 + 2] * inv, o[d4 + 3] * inv};
-    if (a.lse != nullptr) a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = (m_run + log2f(l_run)) * kLn2;
+    if (a.lse != nullptr)
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }
 

@@ -73,6 +73,15 @@ sdpa_status_t check_tensor(const char* name, const void* p, const int64_t* st, i
   return SDPA_OK;
 }
 
+sdpa_status_t check_mask(sdpa_mask_t mask, const int32_t* seq_len_q, const int32_t* seq_len_kv) {
+  if (mask != SDPA_MASK_NONE && mask != SDPA_MASK_CAUSAL && mask != SDPA_MASK_CAUSAL_BOTTOM_RIGHT)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "mask must be SDPA_MASK_NONE, _CAUSAL or _CAUSAL_BOTTOM_RIGHT (got %d)",
+                (int)mask);
+  if ((((uintptr_t)seq_len_q) | ((uintptr_t)seq_len_kv)) % 4 != 0)
+    return fail(SDPA_ERR_NOT_SUPPORTED, "seq_len arrays must be 4-byte aligned");
+  return SDPA_OK;
+}
+
 sdpa_status_t check_sizes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
   if (b < 0 || s_q < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "b=%d and s_q=%d must be >= 0", b, s_q);
   if (h_q < 1 || h_kv < 1 || s_kv < 1 || d < 1)
@@ -121,11 +130,24 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
                        float attn_scale, int causal, sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
                        const sdpa_fp8_scales_t* fp8, hipStream_t stream) {
   g_last_error.clear();
+  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  return sdpa_fwd_ex(q, k, v, o, lse, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride,
+                     attn_scale, causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, in_dtype,
+                     out_dtype, fp8, stream);
+}
+
+sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
+                          int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                          const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
+                          float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
+                          const int32_t* seq_len_kv, sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
+                          const sdpa_fp8_scales_t* fp8, hipStream_t stream) {
+  g_last_error.clear();
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype (%d, %d)", (int)in_dtype, (int)out_dtype);
-  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if ((st = check_mask(mask, seq_len_q, seq_len_kv)) != SDPA_OK) return st;
   if (!(attn_scale > 0.f) || !isfinite(attn_scale))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
   if ((in_dtype == SDPA_FP8_E4M3) != (fp8 != nullptr))
@@ -177,7 +199,10 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
   a.s_q = s_q;
   a.s_kv = s_kv;
   a.d = d;
-  a.causal = causal;
+  a.causal = mask != SDPA_MASK_NONE;
+  a.bottom_right = mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT;
+  a.seq_q = seq_len_q;
+  a.seq_kv = seq_len_kv;
   a.scale = attn_scale;
   if (fp8 != nullptr) {
     a.scale = attn_scale * fp8->descale_q * fp8->descale_k;
@@ -186,8 +211,8 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
     a.descale_p = fp8->descale_p;
   }
   if (log_level() >= 2)
-    fprintf(stderr, "[sdpa] fwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d causal=%d\n", (int)io, d, b, h_q,
-            h_kv, s_q, s_kv, causal);
+    fprintf(stderr, "[sdpa] fwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d lens=%d\n", (int)io, d, b,
+            h_q, h_kv, s_q, s_kv, (int)mask, (seq_len_q != nullptr) + 2 * (seq_len_kv != nullptr));
   if (g_timing.n >= 2) (void)hipEventRecord(g_timing.ev[0], stream);
   hipError_t e;
   switch (io) {
@@ -215,10 +240,26 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
                        float attn_scale, int causal, sdpa_dtype_t dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
+  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  return sdpa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride,
+                     v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, attn_scale,
+                     causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, int b, int h_q, int h_kv, int s_q,
+                          int s_kv, int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                          const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+                          const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4],
+                          float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
+                          const int32_t* seq_len_kv, sdpa_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
   if (!valid_dtype(dtype)) return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
-  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if ((st = check_mask(mask, seq_len_q, seq_len_kv)) != SDPA_OK) return st;
   if (!(attn_scale > 0.f) || !isfinite(attn_scale))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
   if (!((dtype == SDPA_BF16 || dtype == SDPA_F16) && (d == 64 || d == 128)))
@@ -265,7 +306,10 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
   a.s_q = s_q;
   a.s_kv = s_kv;
   a.d = d;
-  a.causal = causal;
+  a.causal = mask != SDPA_MASK_NONE;
+  a.bottom_right = mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT;
+  a.seq_q = seq_len_q;
+  a.seq_kv = seq_len_kv;
   a.scale = attn_scale;
   const size_t need = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
   if (workspace_bytes < need)
@@ -274,8 +318,8 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
   if (((uintptr_t)workspace) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "workspace is not 16-byte aligned");
   a.delta = (float*)workspace;
   if (log_level() >= 2)
-    fprintf(stderr, "[sdpa] bwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d causal=%d\n", (int)io, d, b, h_q,
-            h_kv, s_q, s_kv, causal);
+    fprintf(stderr, "[sdpa] bwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d lens=%d\n", (int)io, d, b,
+            h_q, h_kv, s_q, s_kv, (int)mask, (seq_len_q != nullptr) + 2 * (seq_len_kv != nullptr));
   return hip_status(sdpa::launch_bwd(a, io, stream, g_timing), "backward launch");
 }
 

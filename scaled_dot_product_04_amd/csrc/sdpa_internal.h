@@ -22,6 +22,9 @@ struct FwdArgs {
   Strides3 qs, ks, vs, os;
   int b, h_q, h_kv, s_q, s_kv, d;
   int causal;
+  int bottom_right;        // causal diagonal aligned to the end of the key range
+  const int32_t* seq_q;    // device [b] valid query rows, or null (= s_q)
+  const int32_t* seq_kv;   // device [b] valid keys, or null (= s_kv)
   float scale;  // attn_scale (already multiplied by the fp8 q/k descales for fp8)
   // fp8 only
   float descale_v, scale_p, descale_p;
@@ -40,6 +43,9 @@ struct BwdArgs {
   Strides3 qs, ks, vs, os, dos, dqs, dks, dvs;
   int b, h_q, h_kv, s_q, s_kv, d;
   int causal;
+  int bottom_right;
+  const int32_t* seq_q;
+  const int32_t* seq_kv;
   float scale;
   float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
 };

@@ -132,6 +132,16 @@ def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
     return out
 
 
+def make_lengths(b: int, s: int, seed: int, min_len: int = 0) -> torch.Tensor:
+    """Per-batch valid lengths for the padding mask: int32 [b], uniform in
+    [min_len, s] from a CPU generator seeded with ``seed``; the first entry is
+    s (one unpadded batch element) so that full and padded rows both occur."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.randint(min_len, s + 1, (b,), generator=gen, dtype=torch.int32)
+    lens[0] = s
+    return lens
+
+
 def empty_logical(b: int, h: int, s: int, d: int, layout: str, dtype: str,
                   device="cpu") -> torch.Tensor:
     """Uninitialised (b, h, s, d) view in ``layout`` (for outputs and gradients)."""

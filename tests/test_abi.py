@@ -130,3 +130,43 @@ def test_workspace_size_is_positive_and_monotone():
     assert 0 < small < big
     assert small % 16 == 0 and big % 16 == 0
     assert f(0, 4, 4, 128, 128, 128, 1, sdpa.SDPA_BF16) == 0
+
+
+def _fwd_ex(mask=1, lq=None, lk=None, **kw):
+    lib = sdpa.load_library()
+    S = ctypes.c_int64 * 4
+    st = lib.sdpa_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 2, 64, 64, 128, S(*_bshd(2, 4, 64, 128)),
+                         S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 4, 64, 128)), 0.088,
+                         mask, lq, lk, kw.get("tin", sdpa.SDPA_BF16), sdpa.SDPA_BF16, None, None)
+    return st, lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(mask=3), 1, "mask must be"),
+    (dict(mask=-1), 1, "mask must be"),
+    (dict(lq=FAKE + 2), 2, "4-byte aligned"),
+    (dict(lk=FAKE + 1), 2, "4-byte aligned"),
+    (dict(mask=2, tin=9), 1, "dtype"),
+])
+def test_forward_ex_validation_errors(kw, status, needle):
+    st, msg = _fwd_ex(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_backward_ex_validation_errors():
+    lib = sdpa.load_library()
+    b, hq, hkv, s, d = 2, 4, 2, 64, 128
+    S = ctypes.c_int64 * 4
+    qs, ks = S(*_bshd(b, hq, s, d)), S(*_bshd(b, hkv, s, d))
+
+    def call(mask, lq):
+        st = lib.sdpa_bwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, b, hq, hkv, s, s, d,
+                             qs, ks, ks, qs, qs, qs, ks, ks, 0.088, mask, lq, None, sdpa.SDPA_BF16, FAKE,
+                             1 << 20, None)
+        return st, lib.sdpa_last_error().decode()
+
+    st, msg = call(5, None)
+    assert st == 1 and "mask must be" in msg
+    st, msg = call(2, FAKE + 2)
+    assert st == 2 and "4-byte aligned" in msg

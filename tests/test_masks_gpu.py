@@ -1,0 +1,260 @@
+"""GPU parity of the padding mask (per-batch seq_len_q / seq_len_kv) and the
+bottom-right causal alignment (sdpa_fwd_ex / sdpa_bwd_ex) against the float64
+oracle, for every forward kernel (bf16, f16, f32, fp8) and the backward.
+
+Rows that see no key must come out exactly as O = 0, LSE = -inf, dQ = 0, and
+keys past seq_len_kv exactly as dK = dV = 0; values in the padding must never
+be read (NaN placed there changes nothing)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_04_amd as sdpa
+import sdpa_inputs
+from oracle import attention_backward, attention_forward
+from sdpa_inputs import Workload
+from tests.parity import LSE_REL, TOL, excess_err, f64, max_abs, rel_fro, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+ALIGN = {"none": (False, "top_left"), "causal": (True, "top_left"), "bottom_right": (True, "bottom_right")}
+
+
+def _causal_arg(mask):
+    return {"none": False, "causal": True, "bottom_right": "bottom_right"}[mask]
+
+
+def _fp8_scales(g):
+    return sdpa.Fp8Scales(g["descale_q"], g["descale_k"], g["descale_v"], g["scale_p"], g["descale_p"])
+
+
+def _run_fwd(w, g, mask, lq, lk):
+    fp8 = _fp8_scales(g) if w.dtype == "fp8" else None
+    o, lse = sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=_causal_arg(mask), fp8=fp8,
+                      seq_len_q=None if lq is None else lq.cuda(),
+                      seq_len_kv=None if lk is None else lk.cuda())
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_fwd(w, ins, mask, lq, lk, heads=None, rows=None):
+    causal, align = ALIGN[mask]
+    q = f64(ins["q"], ins.get("descale_q"))
+    k = f64(ins["k"], ins.get("descale_k"))
+    v = f64(ins["v"], ins.get("descale_v"))
+    return attention_forward(q, k, v, w.scale, causal, heads=heads, rows=rows,
+                             seq_len_q=None if lq is None else lq.numpy(),
+                             seq_len_kv=None if lk is None else lk.numpy(), align=align)
+
+
+def _check_lse(lg, lr):
+    m = ~np.isnan(lr)
+    lg, lr = lg[m], lr[m]
+    assert np.array_equal(np.isneginf(lg), np.isneginf(lr)), "rows without keys must have LSE = -inf"
+    fin = np.isfinite(lr)
+    if fin.any():
+        err = np.abs(lg[fin] - lr[fin]) / np.maximum(1.0, np.abs(lr[fin]))
+        assert err.max() <= LSE_REL, f"LSE rel err {err.max():.3e}"
+
+
+def _check_fwd(w, o, lse, o_ref, lse_ref, rows=None):
+    og, lg = f64(o.cpu()), lse.cpu().numpy()
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    tol_key = "fp8" if w.dtype == "fp8" else w.out_dtype
+    exc = excess_err(og, o_ref, w.out_dtype)
+    say(f"    O: max|err|={max_abs(og, o_ref):.3e} beyond-rounding={exc:.3e}")
+    assert exc <= TOL[tol_key], exc
+    empty = np.isneginf(lse_ref)
+    assert (og[empty] == 0).all(), "rows without keys must have O = 0"
+    _check_lse(lg, lse_ref)
+
+
+SHAPES = [(300, 333), (333, 200)]  # s_kv > s_q (positive bottom-right offset) and s_kv < s_q
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bottom_right"])
+@pytest.mark.parametrize("sq_skv", SHAPES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fwd_padding_and_alignment(dtype, d, sq_skv, mask):
+    s_q, s_kv = sq_skv
+    w = Workload("fwd_mask", 3, 4, 2, s_q, s_kv, d, dtype, dtype, mask != "none", 1 / math.sqrt(d), "bshd",
+                 100 + d + s_q)
+    lq = sdpa_inputs.make_lengths(w.b, s_q, w.seed)
+    lk = sdpa_inputs.make_lengths(w.b, s_kv, w.seed + 1)
+    say(f"[mask fwd] {w} mask={mask} lq={lq.tolist()} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, mask, lq, lk)
+    o_ref, lse_ref = _oracle_fwd(w, ins, mask, lq, lk)
+    _check_fwd(w, o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("mask", ["causal", "bottom_right"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_fp8_padding_and_alignment(d, mask):
+    w = Workload("fp8_mask", 3, 4, 2, 333, 270, d, "fp8", "bf16", True, 1 / math.sqrt(d), "bshd", 7 + d)
+    lq = sdpa_inputs.make_lengths(w.b, w.s_q, w.seed)
+    lk = sdpa_inputs.make_lengths(w.b, w.s_kv, w.seed + 1)
+    say(f"[mask fp8] {w} mask={mask} lq={lq.tolist()} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, mask, lq, lk)
+    o_ref, lse_ref = _oracle_fwd(w, ins, mask, lq, lk)
+    _check_fwd(w, o, lse, o_ref, lse_ref)
+    og = f64(o.cpu())
+    assert rel_fro(og, o_ref) <= TOL["fp8"]
+
+
+def _bwd(w, g, o, lse, mask, lq, lk):
+    grads = sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=_causal_arg(mask),
+                     seq_len_q=None if lq is None else lq.cuda(),
+                     seq_len_kv=None if lk is None else lk.cuda())
+    torch.cuda.synchronize()
+    return grads
+
+
+def _oracle_bwd(w, ins, mask, lq, lk):
+    causal, align = ALIGN[mask]
+    q, k, v, do = (f64(ins[n]) for n in ("q", "k", "v", "do"))
+    return attention_backward(q, k, v, do, w.scale, causal, seq_len_q=None if lq is None else lq.numpy(),
+                              seq_len_kv=None if lk is None else lk.numpy(), align=align)
+
+
+def _check_bwd(w, grads, refs, lq, lk):
+    tol = 2 * TOL[w.out_dtype]
+    for name, x, r in zip(("dq", "dk", "dv"), grads, refs):
+        xa = f64(x.cpu())
+        exc = excess_err(xa, r, w.out_dtype)
+        say(f"    {name}: max|err|={max_abs(xa, r):.3e} beyond-rounding={exc:.3e} max|ref|={np.abs(r).max():.2f}")
+        assert exc <= tol, (name, exc)
+        n = lq if name == "dq" else lk
+        for bi in range(w.b):  # padding: exactly zero
+            assert (xa[bi, :, int(n[bi]):] == 0).all(), (name, bi)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bottom_right"])
+@pytest.mark.parametrize("sq_skv", SHAPES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bwd_padding_and_alignment(dtype, d, sq_skv, mask):
+    s_q, s_kv = sq_skv
+    w = Workload("bwd_mask", 3, 4, 2, s_q, s_kv, d, dtype, dtype, mask != "none", 1 / math.sqrt(d), "bshd",
+                 200 + d + s_q, backward=True)
+    lq = sdpa_inputs.make_lengths(w.b, s_q, w.seed)
+    lk = sdpa_inputs.make_lengths(w.b, s_kv, w.seed + 1)
+    say(f"[mask bwd] {w} mask={mask} lq={lq.tolist()} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, mask, lq, lk)
+    grads = _bwd(w, g, o, lse, mask, lq, lk)
+    _check_bwd(w, grads, _oracle_bwd(w, ins, mask, lq, lk), lq, lk)
+
+
+@pytest.mark.parametrize("h_kv", [8, 1])
+def test_bwd_padding_gqa_split_path(h_kv):
+    """GQA/MQA groups small enough to take the split-group (fp32 partial) path."""
+    w = Workload("bwd_mask_gqa", 2, 8, h_kv, 190, 260, 128, "bf16", "bf16", True, 1 / math.sqrt(128), "bhsd",
+                 300 + h_kv, backward=True)
+    lq = sdpa_inputs.make_lengths(w.b, w.s_q, w.seed)
+    lk = sdpa_inputs.make_lengths(w.b, w.s_kv, w.seed + 1)
+    say(f"[mask bwd gqa] {w} lq={lq.tolist()} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, "bottom_right", lq, lk)
+    grads = _bwd(w, g, o, lse, "bottom_right", lq, lk)
+    _check_bwd(w, grads, _oracle_bwd(w, ins, "bottom_right", lq, lk), lq, lk)
+
+
+def test_padding_values_are_never_read():
+    """NaN in every padded row of Q, K, V and dO leaves all outputs unchanged."""
+    w = Workload("poison", 3, 4, 2, 257, 301, 128, "bf16", "bf16", True, 1 / math.sqrt(128), "bshd", 77,
+                 backward=True)
+    lq, lk = torch.tensor([257, 100, 33], dtype=torch.int32), torch.tensor([150, 301, 64], dtype=torch.int32)
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    clean = to_gpu(ins)
+    dirty = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in clean.items()}
+    for bi in range(w.b):
+        for name, n in (("q", lq), ("do", lq), ("k", lk), ("v", lk)):
+            dirty[name][bi, :, int(n[bi]):] = float("nan")
+    outs = []
+    for g in (clean, dirty):
+        o, lse = _run_fwd(w, g, "bottom_right", lq, lk)
+        outs.append((o, lse) + tuple(_bwd(w, g, o, lse, "bottom_right", lq, lk)))
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), outs[0], outs[1]):
+        if name == "lse":
+            assert torch.equal(a, b), name
+        else:
+            assert not torch.isnan(b).any(), name
+            assert torch.equal(a, b), name
+
+
+def test_no_visible_keys_anywhere():
+    """seq_len_kv = 0 for every batch element: O = 0, LSE = -inf, all gradients 0."""
+    w = Workload("empty_keys", 2, 2, 2, 70, 90, 64, "f16", "f16", False, 0.125, "bhsd", 5, backward=True)
+    lk = torch.zeros(2, dtype=torch.int32)
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, "none", None, lk)
+    assert (o == 0).all() and torch.isneginf(lse).all()
+    dq, dk, dv = _bwd(w, g, o, lse, "none", None, lk)
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+def test_ex_entry_points_equal_plain_ones():
+    """sdpa_fwd_ex / sdpa_bwd_ex with the top-left mask and no lengths give
+    bit-identical results to sdpa_fwd / sdpa_bwd."""
+    w = Workload("ex_eq", 2, 4, 2, 300, 300, 128, "bf16", "bf16", True, 1 / math.sqrt(128), "bshd", 9,
+                 backward=True)
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    g = to_gpu(ins)
+    o1, l1 = sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True)
+    full_q = torch.full((w.b,), w.s_q, dtype=torch.int32, device="cuda")
+    full_k = torch.full((w.b,), w.s_kv, dtype=torch.int32, device="cuda")
+    o2, l2 = sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, seq_len_q=full_q, seq_len_kv=full_k)
+    o3, l3 = sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal="bottom_right")  # square: same diagonal
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3) and torch.equal(l1, l3)
+    r1 = sdpa.bwd(g["q"], g["k"], g["v"], o1, g["do"], l1, scale=w.scale, causal=True)
+    r2 = sdpa.bwd(g["q"], g["k"], g["v"], o1, g["do"], l1, scale=w.scale, causal=True, seq_len_q=full_q,
+                  seq_len_kv=full_k)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("s_q", [1, 7, 64])
+def test_bottom_right_decode_shapes(s_q):
+    """A few new queries against a long key range (a KV-cache step), GQA,
+    bottom-right: the last query row sees every key."""
+    w = Workload("decode_br", 2, 16, 2, s_q, 4096, 128, "bf16", "bf16", True, 1 / math.sqrt(128), "bshd",
+                 40 + s_q)
+    lk = torch.tensor([4096, 3000], dtype=torch.int32)
+    say(f"[mask decode] {w} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, "bottom_right", None, lk)
+    o_ref, lse_ref = _oracle_fwd(w, ins, "bottom_right", None, lk)
+    _check_fwd(w, o, lse, o_ref, lse_ref)
+
+
+def test_varlen_full_size_sampled():
+    """hd128 bf16 bottom-right causal at b4 h16 s4096 with per-batch lengths;
+    sampled heads and rows against the oracle, forward and LSE."""
+    w = Workload("varlen_hd128", 4, 16, 16, 4096, 4096, 128, "bf16", "bf16", True, 1 / math.sqrt(128), "bshd",
+                 4096)
+    lq = sdpa_inputs.make_lengths(w.b, w.s_q, w.seed, min_len=1)
+    lk = sdpa_inputs.make_lengths(w.b, w.s_kv, w.seed + 1, min_len=1)
+    say(f"[varlen sampled] {w} lq={lq.tolist()} lk={lk.tolist()}")
+    ins = sdpa_inputs.make_inputs(w)
+    g = to_gpu(ins)
+    o, lse = _run_fwd(w, g, "bottom_right", lq, lk)
+    rng = np.random.default_rng(1)
+    heads = [(0, 0), (1, 7), (2, 15), (3, 3)]
+    rows = sorted(set([0, 1, 127, 128, 4095] + [int(x) for x in rng.integers(0, w.s_q, 24)]
+                      + [int(n) - 1 for n in lq] + [int(n) for n in lq if n < w.s_q]))
+    o_ref, lse_ref = _oracle_fwd(w, ins, "bottom_right", lq, lk, heads=heads, rows=np.array(rows))
+    _check_fwd(w, o, lse, o_ref, lse_ref, rows=rows)
