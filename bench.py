@@ -139,6 +139,37 @@ def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: i
             "pct_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
 
 
+def decode_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
+    """Extra measurement (not part of `value`): a KV-cache step (b8, h_q 32 /
+    h_kv 8, one query row, 32768 keys, d128 bf16), bound by HBM: the K/V bytes
+    read once per KV head over the time, vs the HBM peak. The row-block kernel
+    (which re-reads K/V per query head) is timed beside the split-KV path."""
+    w = sdpa_inputs.kv_cache()
+    ins = sdpa_inputs.make_inputs(w)
+    g = {k: sdpa_inputs.to_device_like(v, "cuda:0") for k, v in ins.items() if isinstance(v, torch.Tensor)}
+    o = sdpa._like_q(g["q"], torch.bfloat16)
+    lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device="cuda:0")
+    n_ws = sdpa.fwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, torch.bfloat16)
+    ws = torch.empty(max(n_ws, 16), dtype=torch.uint8, device="cuda:0")
+    res = {"workload": w.name, "b": w.b, "h_q": w.h_q, "h_kv": w.h_kv, "s_q": w.s_q, "s_kv": w.s_kv, "d": w.d}
+    kv_bytes = 2 * w.b * w.h_kv * w.s_kv * w.d * 2 + 2 * w.b * w.h_q * w.s_q * w.d * 2 + 4 * w.b * w.h_q * w.s_q
+    for name, kw in (("split_kv", {"workspace": ws}), ("row_block", {"split_kv": False})):
+        for _ in range(warmup):
+            sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=False, out=o, lse=lse, stream=stream, **kw)
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, sh)
+        for _ in range(steps):
+            sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=False, out=o, lse=lse, stream=stream, **kw)
+        hip.record(b, sh)
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / steps
+        gbs = kv_bytes / (ms / 1e3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+    res["algorithmic_bytes"] = kv_bytes
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +178,7 @@ def main() -> int:
     ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the extra KV-cache decode measurement")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -247,6 +279,11 @@ def main() -> int:
         fp8 = fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
         log(f"[bench] fp8 forward (b4 h8 s8192 d256, non-causal): {fp8}")
 
+    dec = None
+    if not args.no_decode:
+        dec = decode_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
+        log(f"[bench] KV-cache decode: {dec}")
+
     cpu = None
     if args.cpu_heads > 0:
         cpu = cpu_baseline(w, ins, args.cpu_heads)
@@ -277,6 +314,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "fp8_forward": fp8,
+        "decode_forward": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -142,8 +142,11 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
  * The lengths are read by the kernels (no host synchronisation); values are
  * clamped to [0, s_q] and [0, s_kv]. A query row that sees no key (a row at or
  * past seq_len_q[i], or under bottom-right alignment a row above the shifted
- * diagonal) gets O = 0 and LSE = -inf. sdpa_fwd(..., causal, ...) equals
- * sdpa_fwd_ex(..., causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, NULL, NULL, ...).
+ * diagonal) gets O = 0 and LSE = -inf.
+ *   workspace, workspace_bytes  optional device scratch for the split-KV
+ *               path (see sdpa_fwd_workspace_size); NULL / 0 allowed.
+ * sdpa_fwd(..., causal, ...) equals sdpa_fwd_ex(..., causal ? SDPA_MASK_CAUSAL
+ * : SDPA_MASK_NONE, NULL, NULL, ..., NULL, 0, stream).
  */
 sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                           int b, int h_q, int h_kv, int s_q, int s_kv, int d,
@@ -152,7 +155,27 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           float attn_scale, sdpa_mask_t mask,
                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
                           sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
-                          const sdpa_fp8_scales_t* fp8, hipStream_t stream);
+                          const sdpa_fp8_scales_t* fp8,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace that sdpa_fwd_ex's split-KV path needs for this
+ * shape; 0 when the shape does not take it, or takes it without a workspace.
+ *
+ * The JAX attention codelab (step 9) motivates GQA / MQA by the KV-cache
+ * memory of inference. For few query rows against many keys (s_q <= 64,
+ * s_kv >= 512, ceil(s_q * h_q / h_kv / 32) <= h_q / h_kv; BF16 / F16,
+ * d in {64, 128}) the forward groups every query head of a KV head and every
+ * query position into shared row blocks, so each K/V byte is read once, and
+ * splits the key range over many workgroups; per-split fp32 partials
+ * (O / l and LSE) are merged by a second kernel. sdpa_fwd_ex takes that path
+ * when the workspace is given (workspace_bytes >= this size, 16-byte aligned)
+ * or when this size is 0; with workspace == NULL it runs the row-block kernel
+ * instead (same results within rounding). The split changes only the order in
+ * which each row's softmax sums are associated.
+ */
+size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                               sdpa_dtype_t in_dtype);
 
 /*
  * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned

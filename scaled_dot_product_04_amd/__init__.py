@@ -67,7 +67,9 @@ def load_library() -> ctypes.CDLL:
                              ctypes.POINTER(Fp8Scales), vp]
     lib.sdpa_fwd_ex.restype = ctypes.c_int
     lib.sdpa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp, i, i,
-                                ctypes.POINTER(Fp8Scales), vp]
+                                ctypes.POINTER(Fp8Scales), vp, ctypes.c_size_t, vp]
+    lib.sdpa_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.sdpa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.sdpa_bwd.restype = ctypes.c_int
@@ -140,8 +142,14 @@ def _lens(t, b, device, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, dtype) -> int:
+    """Workspace bytes of the split-KV forward for this shape (0: not needed)."""
+    return int(load_library().sdpa_fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, _DTYPE_CODES[dtype]))
+
+
 def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: bool = True,
-        fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, stream=None):
+        fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, workspace=None,
+        split_kv: bool = True, stream=None):
     """O (and LSE) of fused attention. Returns (out, lse); lse is None in inference mode.
 
     q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d); all on the GPU.
@@ -150,6 +158,10 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     fp8: factors for e4m3 inputs (then out_dtype defaults to bfloat16).
     seq_len_q, seq_len_kv: optional device int32 [b] valid lengths (padding
     mask); rows that see no key get O = 0 and LSE = -inf.
+    workspace: device uint8 buffer for the split-KV path (few query rows,
+    many keys); allocated here when the shape needs one and none is given,
+    unless split_kv is False (then no workspace is passed, and shapes whose
+    split-KV plan needs one run the row-block kernel).
     """
     lib = load_library()
     b, h_q, s_q, d = q.shape
@@ -164,10 +176,15 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     if lse is None and return_lse:
         lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
     fp8_arg = ctypes.byref(fp8) if fp8 is not None else None
-    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None:
+    if workspace is None and fp8 is None and split_kv:
+        n = fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, q.dtype) if q.dtype in _DTYPE_CODES else 0
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None or workspace is not None:
+        ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
         st = lib.sdpa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
                              _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask, lq, lk,
-                             in_code, _DTYPE_CODES[out.dtype], fp8_arg, _stream(stream))
+                             in_code, _DTYPE_CODES[out.dtype], fp8_arg, ws_ptr, ws_n, _stream(stream))
     else:
         st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
                           _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask,
@@ -210,6 +227,6 @@ def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, 
     return dq, dk, dv
 
 
-__all__ = ["fwd", "bwd", "bwd_workspace_size", "load_library", "library_path", "Fp8Scales",
+__all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_workspace_size", "load_library", "library_path", "Fp8Scales",
            "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3", "SDPA_MASK_NONE",
            "SDPA_MASK_CAUSAL", "SDPA_MASK_CAUSAL_BOTTOM_RIGHT"]

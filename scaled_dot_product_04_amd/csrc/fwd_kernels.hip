@@ -51,43 +51,6 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 }
 
 
-// Chunk swizzle of the row-major V tile: row r keeps its 16-byte chunk c at
-// position c ^ vswz<D>(r). The LDS serves a 64-lane 8-byte read in two passes
-// of 32 lanes over 64 banks (256 bytes); in one transposed read, the 32 lanes
-// of a pass touch 4 consecutive rows x 2 column groups of 32 bytes each, and
-// this XOR spreads them over all 16 chunk positions (D = 128: one row per 256
-// bytes, rows 4k..4k+3 shifted by 0, 4, 8, 12 chunks; D = 64: two rows per 256
-// bytes, row pairs shifted by 0 and 4). A pass of 16-byte row stores covers
-// whole rows, which any XOR keeps conflict-free.
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-  return D == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2;
-}
-
-// Lane offsets for transposed operand reads from a swizzled row-major tile of
-// D columns (rows = keys): lane (column 32 db + l % 32, half h) receives rows
-// 16 t + 4 h + 0..3 and 16 t + 8 + 4 h + 0..3 via two ds_read_b64_tr_b16.
-template <int D>
-struct SwzLaneF {
-  int tr_off[D / 32];
-  __device__ __forceinline__ void init(int lane) {
-    const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
-    const int row = 4 * h + (i >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = 32 * db + 16 * (grp & 1) + 4 * (i & 3);
-      tr_off[db] = row * D + (((col >> 3) ^ vswz<D>(row)) * 8) + 4 * ((col >> 2) & 1);
-    }
-  }
-  template <typename V8>
-  __device__ __forceinline__ V8 tr(const uint16_t* tile, int db, int t) const {
-    const uint16_t* p = &tile[tr_off[db] + 16 * t * D];
-    const u32x2 lo = ds_read_tr16(p);
-    const u32x2 hi = ds_read_tr16(p + 8 * D);
-    return __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
-  }
-};
-
 // NW waves per workgroup, 32 query rows per wave.
 template <typename T, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {

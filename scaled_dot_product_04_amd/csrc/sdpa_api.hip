@@ -133,7 +133,14 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
   if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   return sdpa_fwd_ex(q, k, v, o, lse, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride,
                      attn_scale, causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, in_dtype,
-                     out_dtype, fp8, stream);
+                     out_dtype, fp8, nullptr, 0, stream);
+}
+
+size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d, sdpa_dtype_t in_dtype) {
+  if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_kv <= 0 || d <= 0 || h_q % h_kv != 0) return 0;
+  if (in_dtype != SDPA_BF16 && in_dtype != SDPA_F16) return 0;
+  const sdpa::Io io = in_dtype == SDPA_BF16 ? sdpa::Io::BF16 : sdpa::Io::F16;
+  return sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io).ws_bytes;
 }
 
 sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
@@ -141,7 +148,8 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
                           float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
                           const int32_t* seq_len_kv, sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
-                          const sdpa_fp8_scales_t* fp8, hipStream_t stream) {
+                          const sdpa_fp8_scales_t* fp8, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   g_last_error.clear();
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
@@ -213,12 +221,29 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   if (log_level() >= 2)
     fprintf(stderr, "[sdpa] fwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d lens=%d\n", (int)io, d, b,
             h_q, h_kv, s_q, s_kv, (int)mask, (seq_len_q != nullptr) + 2 * (seq_len_kv != nullptr));
+  // Few query rows against many keys: the split-KV path, when its workspace
+  // (if it needs one) is given; otherwise the row-block kernel.
+  const sdpa::DecodePlan plan = sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io);
+  const bool split_kv = plan.use && (plan.ws_bytes == 0 || workspace != nullptr);
+  if (split_kv && plan.ws_bytes > 0) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the split-KV forward needs %zu",
+                  workspace_bytes, plan.ws_bytes);
+    if (((uintptr_t)workspace) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "workspace is not 16-byte aligned");
+  }
+  if (log_level() >= 2 && split_kv)
+    fprintf(stderr, "[sdpa] fwd split-KV: n_split=%d split_keys=%d row_blocks=%d\n", plan.n_split,
+            plan.split_keys, plan.n_rb);
   if (g_timing.n >= 2) (void)hipEventRecord(g_timing.ev[0], stream);
   hipError_t e;
-  switch (io) {
-    case sdpa::Io::F32: e = sdpa::launch_fwd_f32(a, stream); break;
-    case sdpa::Io::FP8: e = sdpa::launch_fwd_fp8(a, stream); break;
-    default: e = sdpa::launch_fwd_mfma(a, io, stream); break;
+  if (split_kv) {
+    e = sdpa::launch_fwd_decode(a, plan, workspace, io, stream);
+  } else {
+    switch (io) {
+      case sdpa::Io::F32: e = sdpa::launch_fwd_f32(a, stream); break;
+      case sdpa::Io::FP8: e = sdpa::launch_fwd_fp8(a, stream); break;
+      default: e = sdpa::launch_fwd_mfma(a, io, stream); break;
+    }
   }
   if (e == hipSuccess && g_timing.n >= 2) e = hipEventRecord(g_timing.ev[1], stream);
   return hip_status(e, "forward launch");

@@ -50,6 +50,22 @@ struct BwdArgs {
   float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
 };
 
+// Split-KV forward (few query rows, many keys): partial results of each key
+// split, merged by a second kernel.
+struct DecodeArgs {
+  int n_split;      // key splits per (batch, KV head, row block)
+  int split_keys;   // keys per split (multiple of the key tile)
+  int n_rb;         // 32-row blocks per KV group (rows = (h_q / h_kv) * s_q)
+  float* part_o;    // [n_split][b][h_q][s_q][d] fp32 O / l per split (n_split > 1)
+  float* part_lse;  // [n_split][b][h_q][s_q] natural-log LSE per split, -inf if empty
+};
+
+struct DecodePlan {
+  bool use;         // the split-KV path applies to this shape
+  int n_split, split_keys, n_rb;
+  size_t ws_bytes;  // workspace it needs (0 when n_split == 1)
+};
+
 // Caller events recorded at kernel boundaries (timing hook); n = 0 disables.
 struct TimingEvents {
   hipEvent_t ev[8];
@@ -62,6 +78,8 @@ enum class Io { F32, F16, BF16, FP8 };
 hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+DecodePlan plan_decode(int b, int h_q, int h_kv, int s_q, int s_kv, int d, Io io);
+hipError_t launch_fwd_decode(const FwdArgs& a, const DecodePlan& p, void* workspace, Io io, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te);
 hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
 

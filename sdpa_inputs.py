@@ -192,6 +192,14 @@ def fp8() -> Workload:
                     1.0 / 16.0, "bshd", 9000)
 
 
+def kv_cache() -> Workload:
+    """One new token per sequence against a 32768-entry KV cache, GQA 32/8
+    (the inference use of shared KV heads in the JAX attention codelab,
+    step 9); with one query row the causal mask removes nothing."""
+    return Workload("kv_cache_decode", 8, 32, 8, 1, 32768, 128, "bf16", "bf16", False, 1 / math.sqrt(128),
+                    "bshd", 32768)
+
+
 def all_workloads() -> list[Workload]:
     return ([tiny(False), tiny(True), gpt2()] + [hd128(s) for s in HD128_SEQS]
             + [gqa(h) for h in (32, 8, 1)] + [fp8()])

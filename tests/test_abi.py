@@ -137,7 +137,7 @@ def _fwd_ex(mask=1, lq=None, lk=None, **kw):
     S = ctypes.c_int64 * 4
     st = lib.sdpa_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 2, 64, 64, 128, S(*_bshd(2, 4, 64, 128)),
                          S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 4, 64, 128)), 0.088,
-                         mask, lq, lk, kw.get("tin", sdpa.SDPA_BF16), sdpa.SDPA_BF16, None, None)
+                         mask, lq, lk, kw.get("tin", sdpa.SDPA_BF16), sdpa.SDPA_BF16, None, None, 0, None)
     return st, lib.sdpa_last_error().decode()
 
 
@@ -170,3 +170,19 @@ def test_backward_ex_validation_errors():
     assert st == 1 and "mask must be" in msg
     st, msg = call(2, FAKE + 2)
     assert st == 2 and "4-byte aligned" in msg
+
+
+def test_forward_workspace_size_selects_split_kv_shapes():
+    f = sdpa.load_library().sdpa_fwd_workspace_size
+    # decode-like: one query row per head against a long KV cache -> split-KV partials
+    assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_BF16) > 0
+    assert f(4, 32, 1, 16, 4096, 64, sdpa.SDPA_F16) > 0
+    assert f(8, 32, 8, 1, 32768, 128, sdpa.SDPA_BF16) > 0
+    # many query rows, short keys, fp32/fp8 inputs, invalid heads: no workspace
+    assert f(2, 16, 16, 8192, 8192, 128, sdpa.SDPA_BF16) == 0
+    assert f(2, 16, 16, 48, 8192, 128, sdpa.SDPA_BF16) == 0  # 2 row blocks per head, G = 1
+    assert f(1, 32, 8, 1, 256, 128, sdpa.SDPA_BF16) == 0
+    assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_F32) == 0
+    assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_FP8_E4M3) == 0
+    assert f(1, 6, 4, 1, 8192, 128, sdpa.SDPA_BF16) == 0
+    assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_BF16) % 16 == 0
