@@ -89,7 +89,8 @@ def cpu_baseline(w, ins, n_heads: int) -> dict:
             "seconds": round(dt, 3)}
 
 
-TRAFFIC_RECORDS = {"bwd_dkdv": "profiles/hd128_causal_s8192_dkdv_hbm_traffic.json"}
+TRAFFIC_RECORDS = {"bwd_dkdv": "profiles/hd128_causal_s8192_dkdv_hbm_traffic.json",
+                   "fwd": "profiles/hd128_causal_s8192_fwd_hbm_traffic.json"}
 
 
 def sources_digest(paths) -> str:
@@ -113,6 +114,50 @@ def measured_traffic(kernel: str):
     if sources_digest(rec["sources"]) != rec["sources_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
+
+
+def write_traffic_record(kernel: str, fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_db: str,
+                         commands: list) -> str:
+    """Build the committed HBM-traffic record of one kernel from four rocprofv3
+    --pmc result databases (FETCH_SIZE and WRITE_SIZE of a bench run, and of
+    `bench.py --copy-reference`). Each counter is averaged per dispatch and
+    scaled so that the 1 GiB copy reads 1 GiB and writes 1 GiB. No GPU use."""
+    import json
+    import sqlite3
+
+    short = {"bwd_dkdv": "bwd_dkdv_kernel<sdpa::Bf16T, 128, true>", "fwd": "fwd_mfma_kernel<sdpa::Bf16T, 128, true, 8>",
+             "bwd_dq": "bwd_dq_kernel<sdpa::Bf16T, 128, true>"}[kernel]
+
+    def per_dispatch(db, counter, name_part=None):
+        c = sqlite3.connect(db)
+        tot = {}
+        for kn, cn, did, v in c.execute("select kernel_name, counter_name, dispatch_id, value from counters_collection"):
+            if cn == counter and (name_part is None or name_part in kn):
+                tot.setdefault((kn, did), 0.0)
+                tot[(kn, did)] += v
+        if name_part is None:  # the copy run: the kernel that moved the most bytes
+            best = max({k[0] for k in tot}, key=lambda n: sum(v for k, v in tot.items() if k[0] == n))
+            tot = {k: v for k, v in tot.items() if k[0] == best}
+        return sum(tot.values()) / len(tot)
+
+    gib_kib = float(1 << 20)
+    fetch_scale = gib_kib / per_dispatch(copy_fetch_db, "FETCH_SIZE")
+    write_scale = gib_kib / per_dispatch(copy_write_db, "WRITE_SIZE")
+    fetch = per_dispatch(fetch_db, "FETCH_SIZE", short)
+    write = per_dispatch(write_db, "WRITE_SIZE", short)
+    sources = ["scaled_dot_product_04_amd/csrc/bwd_kernels.hip" if kernel.startswith("bwd")
+               else "scaled_dot_product_04_amd/csrc/fwd_kernels.hip",
+               "scaled_dot_product_04_amd/csrc/device_common.h", "scaled_dot_product_04_amd/_build.py"]
+    rec = {"kernel": short, "workload": "hd128_causal_s8192 (b2 h16 s8192 d128 bf16 causal BSHD)",
+           "fetch_size_kib_per_launch": round(fetch, 1), "write_size_kib_per_launch": round(write, 1),
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+           "hbm_bytes_per_launch": int(round((fetch * fetch_scale + write * write_scale) * 1024)),
+           "commands": commands, "sources": sources, "sources_sha256": sources_digest(sources)}
+    out = TRAFFIC_RECORDS[kernel]
+    with open(os.path.join(ROOT, out), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return out
 
 
 def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
@@ -179,10 +224,25 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the extra KV-cache decode measurement")
+    ap.add_argument("--traffic-record", nargs=5, metavar=("KERNEL", "FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
+                                                          "COPY_WRITE_DB"),
+                    help="write the HBM-traffic record of KERNEL from rocprofv3 --pmc result databases and exit "
+                         "(no GPU use)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
+    if args.traffic_record:
+        k, f_db, w_db, cf_db, cw_db = args.traffic_record
+        cmds = [f"rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
+                f"--no-fp8 --no-decode",
+                f"rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
+                f"--no-fp8 --no-decode",
+                "rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
+                "rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
+                f"python3 bench.py --traffic-record {k} <fetch db> <write db> <copy fetch db> <copy write db>"]
+        log(f"[bench] wrote {write_traffic_record(k, f_db, w_db, cf_db, cw_db, cmds)}")
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path.", file=sys.stderr)
