@@ -32,7 +32,7 @@ namespace sdpa {
 
 namespace {
 
-constexpr int kKvBlock = 128;  // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kKvBlock = 256;  // keys per dK/dV workgroup (8 waves x 32)
 constexpr int kQTile = 32;     // query rows per dK/dV inner step
 constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
 constexpr int kKTile = 32;     // keys per dQ inner step
@@ -195,23 +195,71 @@ __device__ __forceinline__ V8 read_tr_operand(const uint16_t* tr, int TS, int f,
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-// The workgroup walks (query head of its group slice, query tile) pairs in
-// order; the Q / dO tile of step it+2 is loaded into registers while step it
-// is computed, and written to the other LDS buffer at step it+1.
+// Chunk swizzle of the row-major LDS tiles of the dK/dV kernel (K and V
+// blocks, Q and dO tiles; no row padding): 16-byte chunk c of row r sits at
+// position c ^ bswz<D>(r). Two access patterns meet it. A 16-byte row read
+// (MFMA row operand) by 16 consecutive lanes touches chunk c of 16
+// consecutive rows; a transposed read (ds_read_b64_tr_b16) by 32 lanes
+// touches 4 consecutive rows x 4 consecutive chunks. With 64 banks of 4 bytes,
+// D = 128 (one row per 256 bytes) needs bswz to take 16 distinct values over
+// 16 rows and to give rows 4k..4k+3 distinct values in bits 2-3; D = 64 (two
+// rows per 256 bytes) needs 8 distinct values over the even (and the odd)
+// rows and distinct bit 2 for rows 4k and 4k+2. Both choices below do that.
+template <int D>
+__device__ __forceinline__ int bswz(int r) {
+  return D == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Lane offsets of the transposed operand reads from a bswz tile of D columns:
+// lane (column 32 db + l % 32, half h) receives rows 16 t + 4 h + 0..3 (lo) and
+// 16 t + 8 + 4 h + 0..3 (hi), the rows key_of() assigns to the accumulator
+// registers of S. bswz is invariant under +16 rows but not under +8, so the
+// lo and hi reads carry their own offsets.
+template <int D>
+struct TrLaneB {
+  int lo[D / 32], hi[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
+    const int row = 4 * h + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * (grp & 1) + 4 * (i & 3);
+      lo[db] = row * D + (((col >> 3) ^ bswz<D>(row)) * 8) + 4 * ((col >> 2) & 1);
+      hi[db] = (row + 8) * D + (((col >> 3) ^ bswz<D>(row + 8)) * 8) + 4 * ((col >> 2) & 1);
+    }
+  }
+  template <typename V8>
+  __device__ __forceinline__ V8 tr(const uint16_t* tile, int db, int t) const {
+    const u32x2 l = ds_read_tr16(&tile[lo[db] + 16 * t * D]);
+    const u32x2 u = ds_read_tr16(&tile[hi[db] + 16 * t * D]);
+    return __builtin_bit_cast(V8, u32x4{l.x, l.y, u.x, u.y});
+  }
+};
+
+// KV-stationary dK/dV. A workgroup has 8 waves (two per SIMD) and 256 keys;
+// wave w owns keys 32 w .. 32 w + 31 of the block and accumulates their dK^T,
+// dV^T in VGPRs. The block's K and V rows sit in LDS for the whole kernel
+// (128 KB at d = 128); the workgroup walks (query head of its group slice,
+// 32-row query tile) pairs in order, staging each Q / dO tile (and its LSE
+// and D values) in one LDS buffer; the next pair's tile is loaded into
+// registers while the current one is computed. The transposed Q^T / dO^T
+// operands of dK and dV are read from the same row-major tiles with
+// ds_read_b64_tr_b16.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk, int n_split, float* part) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk, int n_split, float* part) {
   typedef typename T::vec8 V8;
-  typedef BlockTile<kQTile, D> QTile;
   constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int RS = QTile::RS, TS = QTile::TS;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kQTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds_[2][kQTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TS];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][kQTile];
-  __shared__ __attribute__((aligned(16))) float dels[2][kQTile];
-  __shared__ __attribute__((aligned(16))) uint16_t Kb[kKvBlock * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb[kKvBlock * RS];
+  constexpr int NT = 512;
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+  constexpr int KVC = kKvBlock * CH / NT;     // K (and V) block chunks per thread
+  constexpr int QCH = kQTile * CH;            // chunks of one Q (or dO) tile
+  static_assert(KVC * NT == kKvBlock * CH && QCH <= NT, "tile / thread mismatch");
+  __shared__ __attribute__((aligned(16))) uint16_t Kb[kKvBlock * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[kKvBlock * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kQTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds_[kQTile * D];
+  __shared__ __attribute__((aligned(16))) float lse2s[kQTile];
+  __shared__ __attribute__((aligned(16))) float dels[kQTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -235,19 +283,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const uint16_t* kp = (const uint16_t*)a.k + bi * a.ks.b + g * a.ks.h;
   const uint16_t* vp = (const uint16_t*)a.v + bi * a.vs.b + g * a.vs.h;
 
-  // K and V rows of this lane's key, as B operands (K^T, V^T) of S and dP.
-  // The workgroup's K and V rows stay in LDS for the whole kernel (staged once,
-  // row-major); each step reads this wave's rows as the B operands of S and dP.
-  // Keeping them in registers instead would exceed the VGPR budget and make
-  // the compiler move accumulators between register files every step.
+  // Stage the block's K and V rows once (keys at or past lk read as zero).
   {
-    ChunkTile<kKvBlock, D> kv;
-    kv.init(a.ks.s, tid);
-    kv.load(kp, kb * kKvBlock, L.lk, tid);  // keys at or past lk read as zero
-    kv.store(Kb, tid);
-    kv.init(a.vs.s, tid);
-    kv.load(vp, kb * kKvBlock, L.lk, tid);
-    kv.store(Vb, tid);
+    const int k0 = kb * kKvBlock;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
+#pragma unroll
+    for (int i = 0; i < KVC; ++i) {
+      const int c = tid + NT * i;
+      const int r = c / CH, cc = c % CH;
+      const int dst = r * D + ((cc ^ bswz<D>(r)) * 8);
+      *(u32x4*)(&Kb[dst]) = buf_load16(kr, (uint32_t)(r * a.ks.s * 2 + cc * 16));
+      *(u32x4*)(&Vb[dst]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
+    }
   }
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -265,17 +313,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const int n_it = Gs * nq;
   const int hq_base = g * G + sp * Gs;
 
-  QTile qreg, dreg;
-  qreg.init(a.qs.s, tid);
-  dreg.init(a.dos.s, tid);
+  // Per-lane LDS offsets, loop-invariant: this lane's row of the Q / dO tile
+  // (row j) and of the K / V block (row 32 wave + j, the same swizzle since
+  // bswz depends on the row mod 16), chunk 2 t + h.
+  int rowoff_q[NKS], rowoff_k[NKS];
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) {
+    rowoff_q[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
+    rowoff_k[t] = (wave * 32 + j) * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
+  }
+  TrLaneB<D> trl;
+  trl.init(lane);
+
+  // Q / dO tile staging: thread tid < QCH owns chunk (r, cc) of each tile.
+  const bool stager = tid < QCH;
+  const int sr = tid / CH, scc = tid % CH;
+  const uint32_t qoff = (uint32_t)(sr * a.qs.s * 2 + scc * 16);
+  const uint32_t doff = (uint32_t)(sr * a.dos.s * 2 + scc * 16);
+  const int sdst = sr * D + ((scc ^ bswz<D>(sr)) * 8);
+  u32x4 qreg = u32x4{0, 0, 0, 0}, dreg = u32x4{0, 0, 0, 0};
   float lreg = 0.f, creg = 0.f;
   auto load_tile = [&](int it) {
     const int hq = hq_base + it / nq;
     const int q0 = (qt0 + it % nq) * kQTile;
-    const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h;
-    const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h;
-    qreg.load(qp, q0, L.lq, tid);  // rows at or past lq read as zero
-    dreg.load(dop, q0, L.lq, tid);
+    const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h + (int64_t)q0 * a.qs.s;
+    const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)q0 * a.dos.s;
+    if (stager) {  // rows at or past lq read as zero
+      qreg = buf_load16(make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2)), qoff);
+      dreg = buf_load16(make_rsrc(dop, tile_bytes(q0, L.lq, a.dos.s, D, 2)), doff);
+    }
     if (tid < kQTile) {
       const int qi = q0 + tid;
       const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + qi;
@@ -286,30 +352,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       creg = qi < L.lq ? a.delta[row] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
-    qreg.store_rm(Qs[buf], tid);
-    qreg.store_tr(Qt[buf], tid);
-    dreg.store_rm(Ds_[buf], tid);
-    dreg.store_tr(Dt[buf], tid);
-    if (tid < kQTile) {
-      lse2s[buf][tid] = lreg;
-      dels[buf][tid] = creg;
-    }
-  };
 
-  if (n_it > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_it > 1) load_tile(1);
-  }
+  if (n_it > 0) load_tile(0);
   for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
     const int q0 = (qt0 + it % nq) * kQTile;
-    __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
-    if (it + 1 < n_it) {
-      store_tile(buf ^ 1);
-      if (it + 2 < n_it) load_tile(it + 2);
+    __syncthreads();  // every wave is done with the previous tile
+    if (stager) {
+      *(u32x4*)(&Qs[sdst]) = qreg;
+      *(u32x4*)(&Ds_[sdst]) = dreg;
     }
+    if (tid < kQTile) {
+      lse2s[tid] = lreg;
+      dels[tid] = creg;
+    }
+    if (it + 1 < n_it) load_tile(it + 1);
+    __syncthreads();  // this tile is in LDS
     // (Tiles whose queries all precede this wave's keys are not skipped: the
     // mask zeroes them, and a branch here would make the compiler copy the
     // dK/dV accumulators between register files on every iteration.)
@@ -318,10 +375,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < NKS; ++t) {
-      const V8 qa = *(const V8*)(&Qs[buf][j * RS + 16 * t + 8 * h]);
-      s = T::mfma(qa, *(const V8*)(&Kb[(wave * 32 + j) * RS + 16 * t + 8 * h]), s);
-      const V8 da = *(const V8*)(&Ds_[buf][j * RS + 16 * t + 8 * h]);
-      dp = T::mfma(da, *(const V8*)(&Vb[(wave * 32 + j) * RS + 16 * t + 8 * h]), dp);
+      s = T::mfma(*(const V8*)(&Qs[rowoff_q[t]]), *(const V8*)(&Kb[rowoff_k[t]]), s);
+      dp = T::mfma(*(const V8*)(&Ds_[rowoff_q[t]]), *(const V8*)(&Vb[rowoff_k[t]]), dp);
     }
     // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
     const bool need_mask = (q0 + kQTile > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
@@ -336,8 +391,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * h;
-      const f32x4 l4 = *(const f32x4*)(&lse2s[buf][row0]);
-      const f32x4 d4 = *(const f32x4*)(&dels[buf][row0]);
+      const f32x4 l4 = *(const f32x4*)(&lse2s[row0]);
+      const f32x4 d4 = *(const f32x4*)(&dels[row0]);
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -358,10 +413,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
           __builtin_bit_cast(V8, u32x4{dspk[4 * t2], dspk[4 * t2 + 1], dspk[4 * t2 + 2], dspk[4 * t2 + 3]});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const V8 doa = read_tr_operand<V8>(Dt[buf], TS, db * 32 + j, t2, h);
-        dv[db] = T::mfma(doa, pb, dv[db]);
-        const V8 qta = read_tr_operand<V8>(Qt[buf], TS, db * 32 + j, t2, h);
-        dk[db] = T::mfma(qta, sb, dk[db]);
+        dv[db] = T::mfma(trl.template tr<V8>(Ds_, db, t2), pb, dv[db]);
+        dk[db] = T::mfma(trl.template tr<V8>(Qs, db, t2), sb, dk[db]);
       }
     }
   }
@@ -601,9 +654,9 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
   const int n_kblk = (a.s_kv + kKvBlock - 1) / kKvBlock;
   const dim3 g1(n_kblk * a.b * a.h_kv * n_split);
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), g1, dim3(256), 0, stream, a, n_kblk, n_split, part);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), g1, dim3(256), 0, stream, a, n_kblk, n_split, part);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
   if (n_split > 1) {
     const int64_t n4 = (int64_t)a.b * a.h_kv * a.s_kv * D / 4 * 2;
     const int64_t blocks = (n4 + 255) / 256;
