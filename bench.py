@@ -215,6 +215,48 @@ def decode_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps
     return res
 
 
+def varlen_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
+    """Extra measurement (not part of `value`): forward + backward of a ragged
+    batch under the padding mask (8 sequences padded to 8192 rows, h16 d128
+    bf16, causal), counted over the valid rows and keys only, next to the same
+    padded shape run without lengths (every row counted)."""
+    w = sdpa_inputs.varlen()
+    lens = sdpa_inputs.make_lengths(w.b, w.s_q, w.seed, min_len=1)
+    ins = sdpa_inputs.make_inputs(w, with_grad=True)
+    dev = torch.device("cuda:0")
+    g = {k: sdpa_inputs.to_device_like(v, dev) for k, v in ins.items() if isinstance(v, torch.Tensor)}
+    lens_d = lens.to(dev)
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    ws = torch.empty(max(sdpa.bwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, True, torch.bfloat16), 16),
+                     dtype=torch.uint8, device=dev)
+    res = {"workload": w.name, "b": w.b, "h": w.h_q, "s_max": w.s_q, "d": w.d, "lengths": lens.tolist()}
+    per_head = [4.0 * int(n) * int(n) * w.d / 2 for n in lens]  # causal, square per sequence
+    flops_valid = 3.5 * w.h_q * sum(per_head)
+    flops_padded = 3.5 * w.fwd_flops
+    for name, kw in (("padding_mask", {"seq_len_q": lens_d, "seq_len_kv": lens_d}), ("dense", {})):
+        def step():
+            sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, stream=stream, **kw)
+            sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv,
+                     workspace=ws, stream=stream, **kw)
+        for _ in range(warmup):
+            step()
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, sh)
+        for _ in range(steps):
+            step()
+        hip.record(b, sh)
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / steps
+        fl = flops_valid if name == "padding_mask" else flops_padded
+        res[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms / 1e3) / 1e12, 2),
+                     "pct_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    res["valid_fraction_of_flops"] = round(flops_valid / flops_padded, 4)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +266,7 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the extra KV-cache decode measurement")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the extra padding-mask (ragged batch) measurement")
     ap.add_argument("--traffic-record", nargs=5, metavar=("KERNEL", "FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
                                                           "COPY_WRITE_DB"),
                     help="write the HBM-traffic record of KERNEL from rocprofv3 --pmc result databases and exit "
@@ -235,9 +278,9 @@ def main() -> int:
     if args.traffic_record:
         k, f_db, w_db, cf_db, cw_db = args.traffic_record
         cmds = [f"rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
-                f"--no-fp8 --no-decode",
+                f"--no-fp8 --no-decode --no-varlen",
                 f"rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
-                f"--no-fp8 --no-decode",
+                f"--no-fp8 --no-decode --no-varlen",
                 "rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
                 "rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
                 f"python3 bench.py --traffic-record {k} <fetch db> <write db> <copy fetch db> <copy write db>"]
@@ -344,6 +387,11 @@ def main() -> int:
         dec = decode_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
         log(f"[bench] KV-cache decode: {dec}")
 
+    vl = None
+    if not args.no_varlen:
+        vl = varlen_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
+        log(f"[bench] ragged batch (padding mask): {vl}")
+
     cpu = None
     if args.cpu_heads > 0:
         cpu = cpu_baseline(w, ins, args.cpu_heads)
@@ -375,6 +423,7 @@ def main() -> int:
         "roofline": roofline,
         "fp8_forward": fp8,
         "decode_forward": dec,
+        "varlen_forward_backward": vl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -265,12 +265,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const int j = lane & 31, h = lane >> 5;
   const int n_slots = a.b * a.h_kv * n_split;
   // Linear id -> (key block, slot); causal: key block 0 (the most query tiles) first.
+  // The n_split workgroups of one KV group load the same K/V block: one XCD.
   const int kb = blockIdx.x / n_slots;
-  int slot = blockIdx.x - kb * n_slots;
-  if ((n_slots & 7) == 0) {
-    const int per = n_slots >> 3;
-    slot = (slot & 7) * per + (slot >> 3);
-  }
+  const int slot = xcd_slot(blockIdx.x - kb * n_slots, n_slots, n_split);
   const int sp = slot % n_split;
   const int bg = slot / n_split;
   const int g = bg % a.h_kv, bi = bg / a.h_kv;
@@ -497,11 +494,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int rank = blockIdx.x / bh_total;
-  int slot = blockIdx.x - rank * bh_total;
-  if ((bh_total & 7) == 0) {
-    const int per = bh_total >> 3;
-    slot = (slot & 7) * per + (slot >> 3);
-  }
+  const int slot = xcd_slot(blockIdx.x - rank * bh_total, bh_total, a.h_q / a.h_kv);  // KV group: one XCD
   const int qb = n_qblk - 1 - rank;
   const int bi = slot / a.h_q, hq = slot - (slot / a.h_q) * a.h_q;
   const int g = hq / (a.h_q / a.h_kv);

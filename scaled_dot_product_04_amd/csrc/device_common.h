@@ -98,6 +98,19 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 
 // Bytes of rows [row0, n_rows) of a row-major tile with `row_stride` elements
 // between rows and `row_len` elements per row (0 if none), clamped to 2^31.
+// Workgroup ids are dealt round-robin over the 8 XCDs (id % 8), each with its
+// own L2. Maps a dispatch slot s in [0, total) to a work slot such that the
+// `share` consecutive work slots that read the same K/V (the query heads of
+// one KV group, or the splits of one) sit on one XCD and consecutive such
+// groups go to different XCDs, so that unequal groups (a ragged batch) still
+// spread over the whole chip. Identity when total or total / share is not a
+// multiple of 8.
+__device__ __forceinline__ int xcd_slot(int s, int total, int share) {
+  if ((total & 7) != 0 || ((total / share) & 7) != 0) return s;
+  const int x = s & 7, k = s >> 3;
+  return (x + 8 * (k / share)) * share + k % share;
+}
+
 // Lengths of batch element bi under the padding mask: lq valid query rows,
 // lk valid keys (per-batch device arrays, clamped to [0, s]; null = full), and
 // the causal diagonal offset: key j is visible to row i iff j <= i + off, with

@@ -74,11 +74,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_q
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int rank = blockIdx.x / bh_total;
-  int slot = blockIdx.x - rank * bh_total;
-  if ((bh_total & 7) == 0) {
-    const int per = bh_total >> 3;
-    slot = (slot & 7) * per + (slot >> 3);
-  }
+  const int slot = xcd_slot(blockIdx.x - rank * bh_total, bh_total, a.h_q / a.h_kv);  // KV group: one XCD
   const int qb = n_qblk - 1 - rank;
   const int bi = slot / a.h_q, hq = slot - (slot / a.h_q) * a.h_q;
   const int g = hq / (a.h_q / a.h_kv);

@@ -34,17 +34,12 @@ namespace {
 
 
 // Maps a linear workgroup id to (query block, b, head). Query blocks are
-// issued from the last (longest under the causal mask) to the first. When
-// the head count allows, consecutive heads are gathered on one XCD
-// (workgroups are dealt to the 8 XCDs round-robin by id).
-__device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int h_q, int& qb,
-                                          int& bi, int& hq) {
+// issued from the last (longest under the causal mask) to the first; within a
+// rank, the query heads of one KV group share an XCD (xcd_slot).
+__device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int h_q, int G, int& qb, int& bi,
+                                          int& hq) {
   const int rank = id / bh_total;
-  int slot = id - rank * bh_total;
-  if ((bh_total & 7) == 0) {
-    const int per = bh_total >> 3;
-    slot = (slot & 7) * per + (slot >> 3);
-  }
+  const int slot = xcd_slot(id - rank * bh_total, bh_total, G);
   qb = n_qblk - 1 - rank;
   bi = slot / h_q;
   hq = slot - bi * h_q;
@@ -79,7 +74,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
   int qb, bi, hq;
-  map_block(blockIdx.x, n_qblk, a.b * a.h_q, a.h_q, qb, bi, hq);
+  map_block(blockIdx.x, n_qblk, a.b * a.h_q, a.h_q, a.h_q / a.h_kv, qb, bi, hq);
   const int g = hq / (a.h_q / a.h_kv);
   const int qblk0 = qb * BM;
   const int q0 = qblk0 + wave * 32;

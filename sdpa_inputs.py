@@ -200,6 +200,13 @@ def kv_cache() -> Workload:
                     "bshd", 32768)
 
 
+def varlen() -> Workload:
+    """A ragged batch for the padding mask: 8 sequences padded to 8192 rows,
+    h16 d128 bf16, causal; the valid lengths come from make_lengths(8, 8192, 8192)."""
+    return Workload("varlen_hd128", 8, 16, 16, 8192, 8192, 128, "bf16", "bf16", True, 1 / math.sqrt(128),
+                    "bshd", 8192)
+
+
 def all_workloads() -> list[Workload]:
     return ([tiny(False), tiny(True), gpt2()] + [hd128(s) for s in HD128_SEQS]
             + [gqa(h) for h in (32, 8, 1)] + [fp8()])
