@@ -6,6 +6,7 @@ code with the HIP library. Parity status of each function is stated in
 ``sdpa_oracle``'s docstrings and pinned by ``tests/test_oracle.py``.
 """
 from .sdpa_oracle import (  # noqa: F401
+    alibi_slopes,
     attention_backward,
     attention_forward,
     attention_probs,

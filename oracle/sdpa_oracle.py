@@ -38,6 +38,11 @@ design notes of the repository):
   offset uses those lengths. A query row that sees no key (a padded row, or a
   row above a bottom-right diagonal) has O = 0 and LSE = -inf and takes no
   part in the backward (its dQ is 0 and it adds nothing to dK, dV).
+* score modifiers (the node's ``bias`` and ``use_alibi_mask`` options, also
+  without semantics on the pages): an additive bias B[b, h, i, j] and an
+  ALiBi term -slope[h] * |i + off - j| (off as for the causal diagonal, 0
+  without a causal mask) are added to the scaled scores before the mask and
+  the softmax; the bias is a constant (no gradient is formed for it).
 * the backward is the exact gradient of the forward (the pages only show that
   a forward+backward exists), with D_i = sum_d dO_id * O_id.
 * fp8 inputs are the e4m3 codes times a per-tensor fp32 descale; the oracle
@@ -80,13 +85,21 @@ def _lengths(bi: int, s_q: int, s_kv: int, causal: bool, align: str, seq_len_q, 
 
 
 def _masked_scores(q_rows: np.ndarray, row_idx: np.ndarray, kh: np.ndarray, scale: float,
-                   causal: bool, lq: int = None, lk: int = None, off: int = 0) -> np.ndarray:
-    """S = scale * Q K^T for the given query rows, with masked entries set to -inf.
+                   causal: bool, lq: int = None, lk: int = None, off: int = 0, bias_rows=None,
+                   slope: float = None) -> np.ndarray:
+    """S = scale * Q K^T (+ bias + ALiBi) for the given query rows, with masked
+    entries set to -inf.
 
+    bias_rows: optional additive bias for these rows (n_rows x n_keys).
+    slope: optional ALiBi slope of this head: adds -slope * |i + off - j|.
     Masked: keys j >= lk, every key of a row i >= lq, and (causal) j > i + off.
     """
     s = scale * (q_rows @ kh.T)
     key_idx = np.arange(kh.shape[0])
+    if bias_rows is not None:
+        s = s + bias_rows
+    if slope is not None:
+        s = s - slope * np.abs(row_idx[:, None] + off - key_idx[None, :])
     lq = np.iinfo(np.int64).max if lq is None else lq
     lk = kh.shape[0] if lk is None else lk
     vis = (key_idx[None, :] < lk) & (row_idx[:, None] < lq)
@@ -110,9 +123,19 @@ def _softmax_rows(s: np.ndarray):
     return p, np.where(empty, -np.inf, m[:, 0]), l[:, 0]
 
 
+def _bias_rows(bias, bi, hq, ridx, lk):
+    """Rows ridx of the additive bias of (bi, hq), keys < lk; bias is
+    (b or 1, h or 1, s_q, s_kv) and broadcasts over its size-1 dims."""
+    if bias is None:
+        return None
+    bb = bias[bi if bias.shape[0] > 1 else 0, hq if bias.shape[1] > 1 else 0]
+    return np.asarray(bb[ridx, :lk], dtype=np.float64)
+
+
 def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                       causal: bool, heads=None, rows=None, row_block: int = _ROW_BLOCK,
-                      seq_len_q=None, seq_len_kv=None, align: str = "top_left"):
+                      seq_len_q=None, seq_len_kv=None, align: str = "top_left", bias=None,
+                      alibi_slopes=None):
     """Forward pass O = softmax(scale * Q K^T + mask) V and LSE, in float64.
 
     Follows the JAX attention codelab's step 1 formula and step 4 dense form
@@ -126,6 +149,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     seq_len_q, seq_len_kv: optional per-batch valid lengths (padding mask),
     clamped to [0, s_q] and [0, s_kv]; align: "top_left" or "bottom_right"
     placement of the causal diagonal.
+    bias: optional additive bias (b or 1, h_q or 1, s_q, s_kv); alibi_slopes:
+    optional per-query-head ALiBi slopes (h_q,).
     Returns (O, LSE): O has shape (b, h_q, n_rows, d) and LSE (b, h_q, n_rows);
     entries for heads not in ``heads`` are NaN. Rows that see no key have
     O = 0 and LSE = -inf.
@@ -145,7 +170,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         for r0 in range(0, n, row_block):
             ridx = row_idx_all[r0:r0 + row_block]
             qr = np.asarray(q[bi, hq][ridx], dtype=np.float64)
-            s = _masked_scores(qr, ridx, kh, scale, causal, lq, lk, off)
+            slope = None if alibi_slopes is None else float(alibi_slopes[hq])
+            s = _masked_scores(qr, ridx, kh, scale, causal, lq, lk, off, _bias_rows(bias, bi, hq, ridx, lk), slope)
             p, m, l = _softmax_rows(s)
             out[bi, hq, r0:r0 + len(ridx)] = p @ vh
             with np.errstate(divide="ignore"):  # ln 0 = -inf for rows that see no key
@@ -154,7 +180,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-                    seq_len_q=None, seq_len_kv=None, align: str = "top_left") -> np.ndarray:
+                    seq_len_q=None, seq_len_kv=None, align: str = "top_left", bias=None,
+                    alibi_slopes=None) -> np.ndarray:
     """The full attention-weight tensor P (b, h_q, s_q, s_kv); small inputs only.
 
     The "weights" of the JAX attention codelab's step 1 (rows sum to one; a
@@ -167,15 +194,17 @@ def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
         lq, lk, off = _lengths(bi, s_q, s_kv, causal, align, seq_len_q, seq_len_kv)
         for hq in range(h_q):
             kh = np.asarray(k[bi, _kv_head(hq, h_q, h_kv), :lk], dtype=np.float64)
+            slope = None if alibi_slopes is None else float(alibi_slopes[hq])
             s = _masked_scores(np.asarray(q[bi, hq], dtype=np.float64), np.arange(s_q), kh,
-                               scale, causal, lq, lk, off)
+                               scale, causal, lq, lk, off, _bias_rows(bias, bi, hq, np.arange(s_q), lk), slope)
             p_all[bi, hq, :, :lk] = _softmax_rows(s)[0]
     return p_all
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                        scale: float, causal: bool, kv_heads=None, row_block: int = _ROW_BLOCK,
-                       seq_len_q=None, seq_len_kv=None, align: str = "top_left"):
+                       seq_len_q=None, seq_len_kv=None, align: str = "top_left", bias=None,
+                       alibi_slopes=None):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for the forward above, in float64.
 
     The pages show only that a forward+backward SDPA exists (the cuDNN 9 blog,
@@ -195,6 +224,7 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
     other entries are NaN. dQ is filled for the query heads of those groups.
     seq_len_q, seq_len_kv, align: as in ``attention_forward``; rows that see
     no key have P = 0, hence dQ = 0 and no contribution to dK, dV.
+    bias, alibi_slopes: as in ``attention_forward``; they only change P.
     """
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
@@ -217,7 +247,9 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
             for r0 in range(0, lq, row_block):  # rows past lq are never read; their dQ is 0
                 ridx = np.arange(r0, min(lq, r0 + row_block))
                 qr, dor = qh[ridx], doh[ridx]
-                p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal, lq, lk, off))
+                slope = None if alibi_slopes is None else float(alibi_slopes[hq])
+                p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal, lq, lk, off,
+                                                       _bias_rows(bias, bi, hq, ridx, lk), slope))
                 o = p @ vh
                 dvec = (dor * o).sum(axis=1)
                 dv_g[:lk] += p.T @ dor
@@ -229,6 +261,20 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
         dk[bi, g] = dk_g
         dv[bi, g] = dv_g
     return dq, dk, dv
+
+
+def alibi_slopes(h: int) -> np.ndarray:
+    """The ALiBi paper's per-head slopes (Press et al., "Train Short, Test
+    Long"): for h a power of two, the geometric sequence 2^(-8/h), 2^(-16/h),
+    ..., 2^(-8); otherwise the slopes of the next lower power of two n followed
+    by every other slope of 2n."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (i + 1) / n) for i in range(n)]
+    n = 1 << (h.bit_length() - 1)
+    out = pow2(n)
+    if n < h:
+        out += pow2(2 * n)[0::2][: h - n]
+    return np.array(out, dtype=np.float64)
 
 
 def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
@@ -264,7 +310,7 @@ def sdpa_flops(b: int, h_q: int, s_q: int, s_kv: int, d: int, causal: bool) -> f
 
 
 __all__ = [
-    "attention_forward", "attention_backward", "attention_probs",
+    "attention_forward", "attention_backward", "attention_probs", "alibi_slopes",
     "fp8_e4m3_decode", "fp8_dequantize", "sdpa_flops",
 ]
 
