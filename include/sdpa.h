@@ -97,6 +97,31 @@ typedef enum {
   SDPA_MASK_CAUSAL_BOTTOM_RIGHT = 2
 } sdpa_mask_t;
 
+/*
+ * Score modifiers of sdpa_fwd_ex / sdpa_bwd_ex: the SDPA node's `bias` and
+ * `use_alibi_mask` options in the cuDNN 9 blog's "SDPA usage" call (the pages
+ * give no semantics; both are added to the scaled scores before the mask):
+ *     S_ij = attn_scale * q_i . k_j + bias[b][h][i][j] - alibi_slopes[h] * |i + off - j|
+ * with off the causal diagonal offset (lk - lq for SDPA_MASK_CAUSAL_BOTTOM_RIGHT,
+ * else 0). Either member may be NULL. The bias is a constant: the backward
+ * forms no gradient for it.
+ *   alibi_slopes  device fp32 [h_q], 4-byte aligned (the ALiBi paper's slopes are
+ *                 2^(-8 (h+1) / h_q) for h_q a power of two).
+ *   bias          device tensor, logical [b][h_q][s_q][s_kv], 16-byte aligned.
+ *   bias_dtype    SDPA_F32, or the io dtype (F16 / BF16 inputs).
+ *   bias_stride   element strides in (b, h, s_q, s_kv) order; the s_kv stride
+ *                 must be 1; 0 broadcasts over b or h; the s_q stride must be a
+ *                 multiple of 16 bytes' worth of elements.
+ * Not supported with FP8 inputs (SDPA_ERR_NOT_SUPPORTED); the split-KV forward
+ * path is not taken when modifiers are present.
+ */
+typedef struct {
+  const float* alibi_slopes;
+  const void* bias;
+  sdpa_dtype_t bias_dtype;
+  int64_t bias_stride[4];
+} sdpa_score_mod_t;
+
 typedef struct {
   float descale_q;
   float descale_k;
@@ -143,10 +168,11 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
  * clamped to [0, s_q] and [0, s_kv]. A query row that sees no key (a row at or
  * past seq_len_q[i], or under bottom-right alignment a row above the shifted
  * diagonal) gets O = 0 and LSE = -inf.
+ *   mod         optional score modifiers (bias tensor, ALiBi slopes); NULL = none.
  *   workspace, workspace_bytes  optional device scratch for the split-KV
  *               path (see sdpa_fwd_workspace_size); NULL / 0 allowed.
  * sdpa_fwd(..., causal, ...) equals sdpa_fwd_ex(..., causal ? SDPA_MASK_CAUSAL
- * : SDPA_MASK_NONE, NULL, NULL, ..., NULL, 0, stream).
+ * : SDPA_MASK_NONE, NULL, NULL, NULL, ..., NULL, 0, stream).
  */
 sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                           int b, int h_q, int h_kv, int s_q, int s_kv, int d,
@@ -154,6 +180,7 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           const int64_t v_stride[4], const int64_t o_stride[4],
                           float attn_scale, sdpa_mask_t mask,
                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                          const sdpa_score_mod_t* mod,
                           sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
                           const sdpa_fp8_scales_t* fp8,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -214,8 +241,9 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
  * be those of the forward that produced o and lse (same meaning and clamping as
  * in sdpa_fwd_ex). Rows that see no key (LSE = -inf) take no part: their dQ is
  * 0 and they add nothing to dK, dV; keys at or past seq_len_kv[i] get
- * dK = dV = 0; dQ rows at or past seq_len_q[i] are 0. The workspace size is
- * that of sdpa_bwd_workspace_size for the same shape.
+ * dK = dV = 0; dQ rows at or past seq_len_q[i] are 0. `mod` must be the
+ * forward's (it changes P). The workspace size is that of
+ * sdpa_bwd_workspace_size for the same shape.
  */
 sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse,
@@ -227,6 +255,7 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
                           const int64_t dk_stride[4], const int64_t dv_stride[4],
                           float attn_scale, sdpa_mask_t mask,
                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                          const sdpa_score_mod_t* mod,
                           sdpa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 

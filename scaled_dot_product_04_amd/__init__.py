@@ -37,6 +37,12 @@ class Fp8Scales(ctypes.Structure):
                 ("descale_p", ctypes.c_float)]
 
 
+class ScoreMod(ctypes.Structure):
+    """sdpa_score_mod_t: optional ALiBi slopes and additive bias tensor."""
+    _fields_ = [("alibi_slopes", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int),
+                ("bias_stride", ctypes.c_int64 * 4)]
+
+
 class SdpaError(RuntimeError):
     """A libsdpa call returned a non-OK status."""
 
@@ -66,8 +72,8 @@ def load_library() -> ctypes.CDLL:
     lib.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, i, i,
                              ctypes.POINTER(Fp8Scales), vp]
     lib.sdpa_fwd_ex.restype = ctypes.c_int
-    lib.sdpa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp, i, i,
-                                ctypes.POINTER(Fp8Scales), vp, ctypes.c_size_t, vp]
+    lib.sdpa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp,
+                                ctypes.POINTER(ScoreMod), i, i, ctypes.POINTER(Fp8Scales), vp, ctypes.c_size_t, vp]
     lib.sdpa_fwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
@@ -78,8 +84,8 @@ def load_library() -> ctypes.CDLL:
                              ctypes.c_size_t, vp]
     lib.sdpa_bwd_ex.restype = ctypes.c_int
     lib.sdpa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
-                                i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, vp, vp, i, vp,
-                                ctypes.c_size_t, vp]
+                                i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, vp, vp,
+                                ctypes.POINTER(ScoreMod), i, vp, ctypes.c_size_t, vp]
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -142,14 +148,51 @@ def _lens(t, b, device, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, device):
+    """Build the sdpa_score_mod_t for an optional bias tensor (b or 1, h_q or 1,
+    s_q, s_kv) and optional fp32 ALiBi slopes (h_q,), or None."""
+    if bias is None and alibi_slopes is None:
+        return None
+    m = ScoreMod()
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (h_q,) or \
+                not alibi_slopes.is_contiguous() or alibi_slopes.device != device:
+            raise ValueError(f"alibi_slopes must be a contiguous float32 tensor of shape ({h_q},) on {device}")
+        m.alibi_slopes = alibi_slopes.data_ptr()
+    if bias is not None:
+        if bias.dim() != 4 or bias.shape[0] not in (1, b) or bias.shape[1] not in (1, h_q) or \
+                tuple(bias.shape[2:]) != (s_q, s_kv) or bias.device != device:
+            raise ValueError(f"bias must be ({b} or 1, {h_q} or 1, {s_q}, {s_kv}) on {device}")
+        st = list(bias.stride())
+        for dim in (0, 1):
+            if bias.shape[dim] == 1:
+                st[dim] = 0
+        m.bias = bias.data_ptr()
+        m.bias_dtype = _DTYPE_CODES[bias.dtype]
+        m.bias_stride = _Strides(*st)
+    return m
+
+
+def alibi_slopes(h: int, device="cuda") -> torch.Tensor:
+    """The ALiBi paper's per-head slopes (power-of-two head counts: 2^(-8 (i+1) / h);
+    otherwise the next lower power of two followed by every other slope of twice that)."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (i + 1) / n) for i in range(n)]
+    n = 1 << (h.bit_length() - 1)
+    out = pow2(n)
+    if n < h:
+        out += pow2(2 * n)[0::2][: h - n]
+    return torch.tensor(out, dtype=torch.float32, device=device)
+
+
 def fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, dtype) -> int:
     """Workspace bytes of the split-KV forward for this shape (0: not needed)."""
     return int(load_library().sdpa_fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, _DTYPE_CODES[dtype]))
 
 
 def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: bool = True,
-        fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, workspace=None,
-        split_kv: bool = True, stream=None):
+        fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, bias=None,
+        alibi_slopes=None, workspace=None, split_kv: bool = True, stream=None):
     """O (and LSE) of fused attention. Returns (out, lse); lse is None in inference mode.
 
     q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d); all on the GPU.
@@ -158,6 +201,8 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     fp8: factors for e4m3 inputs (then out_dtype defaults to bfloat16).
     seq_len_q, seq_len_kv: optional device int32 [b] valid lengths (padding
     mask); rows that see no key get O = 0 and LSE = -inf.
+    bias, alibi_slopes: optional score modifiers added to the scaled scores
+    (bias (b or 1, h_q or 1, s_q, s_kv), fp32 or q's dtype; slopes fp32 (h_q,)).
     workspace: device uint8 buffer for the split-KV path (few query rows,
     many keys); allocated here when the shape needs one and none is given,
     unless split_kv is False (then no workspace is passed, and shapes whose
@@ -169,6 +214,7 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     in_code = _DTYPE_CODES[q.dtype]
     mask = _mask_code(causal)
     lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
+    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device)
     if out_dtype is None:
         out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if out is None:
@@ -180,11 +226,13 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
         n = fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, q.dtype) if q.dtype in _DTYPE_CODES else 0
         if n > 0:
             workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None or workspace is not None:
+    if (mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None or workspace is not None
+            or mod is not None):
         ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
         st = lib.sdpa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
                              _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask, lq, lk,
-                             in_code, _DTYPE_CODES[out.dtype], fp8_arg, ws_ptr, ws_n, _stream(stream))
+                             ctypes.byref(mod) if mod is not None else None, in_code, _DTYPE_CODES[out.dtype],
+                             fp8_arg, ws_ptr, ws_n, _stream(stream))
     else:
         st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h_q, h_kv, s_q, s_kv, d,
                           _strides(q), _strides(k), _strides(v), _strides(out), float(scale), mask,
@@ -199,16 +247,18 @@ def bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, dtype) -> int:
 
 
 def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, dv=None,
-        workspace=None, seq_len_q=None, seq_len_kv=None, stream=None):
+        workspace=None, seq_len_q=None, seq_len_kv=None, bias=None, alibi_slopes=None, stream=None):
     """(dQ, dK, dV) of L = sum(O * dO). dK/dV are summed over each KV head's query group.
 
-    causal, seq_len_q, seq_len_kv: those of the forward that produced o and lse.
+    causal, seq_len_q, seq_len_kv, bias, alibi_slopes: those of the forward that
+    produced o and lse.
     """
     lib = load_library()
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
     mask = _mask_code(causal)
     lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
+    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device)
     dq = _like_q(q, q.dtype) if dq is None else dq
     dk = _like_q(k, k.dtype) if dk is None else dk
     dv = _like_q(v, v.dtype) if dv is None else dv
@@ -219,14 +269,14 @@ def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, 
             b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v), _strides(o),
             _strides(dout), _strides(dq), _strides(dk), _strides(dv), float(scale))
     tail = (_DTYPE_CODES[q.dtype], _ptr(workspace), workspace.numel(), _stream(stream))
-    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None:
-        st = lib.sdpa_bwd_ex(*args, mask, lq, lk, *tail)
+    if mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT or lq is not None or lk is not None or mod is not None:
+        st = lib.sdpa_bwd_ex(*args, mask, lq, lk, ctypes.byref(mod) if mod is not None else None, *tail)
     else:
         st = lib.sdpa_bwd(*args, mask, *tail)
     _check(st)
     return dq, dk, dv
 
 
-__all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_workspace_size", "load_library", "library_path", "Fp8Scales",
+__all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_workspace_size", "alibi_slopes", "ScoreMod", "load_library", "library_path", "Fp8Scales",
            "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3", "SDPA_MASK_NONE",
            "SDPA_MASK_CAUSAL", "SDPA_MASK_CAUSAL_BOTTOM_RIGHT"]

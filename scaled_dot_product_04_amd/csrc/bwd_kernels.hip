@@ -245,7 +245,7 @@ struct TrLaneB {
 // registers while the current one is computed. The transposed Q^T / dO^T
 // operands of dK and dV are read from the same row-major tiles with
 // ds_read_b64_tr_b16.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MOD>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk, int n_split, float* part) {
   typedef typename T::vec8 V8;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -384,6 +384,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
       }
     }
+    // Score modifiers of this (query head, query row, key), log2 units.
+    float madd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) madd[r] = 0.f;
+    if (MOD) {
+      const int hq = hq_base + it / nq;
+      const float slope2 = a.mod.slopes != nullptr ? a.mod.slopes[hq] * kLog2e : 0.f;
+      const char* bias_bh =
+          a.mod.bias != nullptr
+              ? (const char*)a.mod.bias + (bi * a.mod.bb + hq * a.mod.bh) * (a.mod.bias_f32 ? 4 : 2)
+              : nullptr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + acc_row(r, h);
+        const void* brow = (bias_bh != nullptr && qi < a.s_q)
+                               ? (const void*)(bias_bh + (int64_t)qi * a.mod.bs * (a.mod.bias_f32 ? 4 : 2))
+                               : nullptr;
+        madd[r] = fmaf(bias1<T>(brow, a.mod.bias_f32, my_key, a.s_kv), kLog2e,
+                       -slope2 * fabsf((float)(qi + L.off - my_key)));
+      }
+    }
     uint32_t ppk[8], dspk[8];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, -l4[e]));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, madd[4 * r4 + e] - l4[e]));
         pv[e] = p;
         dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
       }
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split,
 // Pipelined like the forward: the K/V tile of step t+2 is loaded into
 // registers while step t is computed and written to the other LDS buffer
 // (K row-major and transposed, V row-major) at step t+1.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MOD>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   typedef typename T::vec8 V8;
   typedef BlockTile<kKTile, D> KTile;
@@ -525,6 +546,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   const float lse = my_q < L.lq ? a.lse[row_bh + my_q] : 0.f;
   const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
   const float dl = my_q < L.lq ? a.delta[row_bh + my_q] : 0.f;
+  const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
+  const void* bias_row =
+      (MOD && a.mod.bias != nullptr && my_q < a.s_q)
+          ? (const void*)((const char*)a.mod.bias +
+                          (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * (a.mod.bias_f32 ? 4 : 2))
+          : nullptr;
   const float sl2 = a.scale * kLog2e;
 
   f32x16 dq[NDB];
@@ -584,13 +611,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
           if (key >= L.lk || (CAUSAL && key > my_q + L.off)) s[nb][r] = -INFINITY;
         }
     }
+    // Score modifiers of this query row and the tile's keys, log2 units.
+    float madd[NSB][16];
+#pragma unroll
+    for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) madd[nb][r] = 0.f;
+    if (MOD) {
+#pragma unroll
+      for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
+          const f32x4 bv = bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            madd[nb][4 * q4 + e] = fmaf(bv[e], kLog2e, -slope2 * fabsf((float)(my_q + L.off - (key0 + e))));
+        }
+    }
     uint32_t dspk[NSB][8];
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, -lse2));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, -lse2));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, madd[nb][r] - lse2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, madd[nb][r + 1] - lse2));
         dspk[nb][r / 2] = pack2<T>(p0 * (dp[nb][r] - dl), p1 * (dp[nb][r + 1] - dl));
       }
     // dQ^T += K^T dS^T
@@ -633,7 +678,7 @@ int choose_split(int b, int h_q, int h_kv, int s_kv) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <typename T, int D>
+template <typename T, int D, bool MOD>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& te) {
   constexpr int RPB = 256 / (D / 8);
   const bool timed = te.n >= 4;
@@ -647,9 +692,9 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
   const int n_kblk = (a.s_kv + kKvBlock - 1) / kKvBlock;
   const dim3 g1(n_kblk * a.b * a.h_kv * n_split);
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, MOD>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, MOD>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
   if (n_split > 1) {
     const int64_t n4 = (int64_t)a.b * a.h_kv * a.s_kv * D / 4 * 2;
     const int64_t blocks = (n4 + 255) / 256;
@@ -660,9 +705,9 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
   const int n_qblk = (a.s_q + kQBlock - 1) / kQBlock;
   const dim3 g2(n_qblk * a.b * a.h_q);
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), g2, dim3(256), 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), g2, dim3(256), 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
   if (timed) (void)hipEventRecord(te.ev[3], stream);
   return hipGetLastError();
 }
@@ -684,10 +729,16 @@ hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
+template <bool MOD>
+hipError_t launch_bwd_m(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
   if (io == Io::BF16)
-    return a.d == 64 ? launch_all<Bf16T, 64>(a, stream, te) : launch_all<Bf16T, 128>(a, stream, te);
-  return a.d == 64 ? launch_all<F16T, 64>(a, stream, te) : launch_all<F16T, 128>(a, stream, te);
+    return a.d == 64 ? launch_all<Bf16T, 64, MOD>(a, stream, te) : launch_all<Bf16T, 128, MOD>(a, stream, te);
+  return a.d == 64 ? launch_all<F16T, 64, MOD>(a, stream, te) : launch_all<F16T, 128, MOD>(a, stream, te);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
+  if (a.mod.slopes != nullptr || a.mod.bias != nullptr) return launch_bwd_m<true>(a, io, stream, te);
+  return launch_bwd_m<false>(a, io, stream, te);
 }
 
 }  // namespace sdpa

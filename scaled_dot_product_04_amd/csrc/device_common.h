@@ -207,4 +207,32 @@ struct SwzLaneF {
   }
 };
 
+// Score modifiers, in natural-log units (the caller multiplies by log2 e).
+// bias_row points at bias[b][h][i][0] of one query row i (null: no bias).
+// Four consecutive keys key..key+3 of that row; keys past n_keys read as 0
+// (they are masked anyway; the guard only keeps the reads in bounds).
+template <typename T>
+__device__ __forceinline__ f32x4 bias4(const void* bias_row, int bias_f32, int key, int n_keys) {
+  f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (bias_row == nullptr) return r;
+  if (key + 3 < n_keys) {
+    if (bias_f32) return *(const f32x4*)((const float*)bias_row + key);
+    const u32x2 w = *(const u32x2*)((const uint16_t*)bias_row + key);
+    return f32x4{to_f32<T>((uint16_t)(w.x & 0xffff)), to_f32<T>((uint16_t)(w.x >> 16)),
+                 to_f32<T>((uint16_t)(w.y & 0xffff)), to_f32<T>((uint16_t)(w.y >> 16))};
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (key + e < n_keys)
+      r[e] = bias_f32 ? ((const float*)bias_row)[key + e] : to_f32<T>(((const uint16_t*)bias_row)[key + e]);
+  return r;
+}
+
+// One bias value bias[row][key] (null row or out of range: 0).
+template <typename T>
+__device__ __forceinline__ float bias1(const void* bias_row, int bias_f32, int key, int n_keys) {
+  if (bias_row == nullptr || key >= n_keys) return 0.f;
+  return bias_f32 ? ((const float*)bias_row)[key] : to_f32<T>(((const uint16_t*)bias_row)[key]);
+}
+
 }  // namespace sdpa

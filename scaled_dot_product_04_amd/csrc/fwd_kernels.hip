@@ -46,8 +46,9 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 }
 
 
-// NW waves per workgroup, 32 query rows per wave.
-template <typename T, int D, bool CAUSAL, int NW>
+// NW waves per workgroup, 32 query rows per wave. MOD: score modifiers
+// (bias tensor and/or ALiBi) are added to the scaled scores.
+template <typename T, int D, bool CAUSAL, int NW, bool MOD>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
   typedef typename T::elem E;
   typedef typename T::vec8 V8;
@@ -102,6 +103,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   float m_run = -INFINITY;  // running max, in log2 units of the scaled scores
   float l_run = 0.f;        // running sum (this lane half's keys only)
   const float sl2 = a.scale * kLog2e;
+  // With modifiers the scores are scaled (and shifted) as soon as they are
+  // computed, so the row max and the exponent use them as they are.
+  const float sc = MOD ? 1.f : sl2;
+  const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
+  const void* bias_row =
+      (MOD && a.mod.bias != nullptr && my_q < a.s_q)
+          ? (const void*)((const char*)a.mod.bias +
+                          (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * (a.mod.bias_f32 ? 4 : 2))
+          : nullptr;
 
   // Keys visible to some row of this block: below lk and, under the causal
   // mask, at most (last valid row) + off.
@@ -176,6 +186,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
       }
     }
+    if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
+#pragma unroll
+      for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
+          const f32x4 bv = bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
+            sacc[nb][4 * q4 + e] = fmaf(sacc[nb][4 * q4 + e], sl2, fmaf(bv[e], kLog2e, -slope2 * dist));
+          }
+        }
+    }
     // Causal / key-length mask (only tiles that cross the diagonal or lk).
     const bool need_mask = (k0 + kBN > L.lk) || (CAUSAL && k0 + kBN - 1 > q0 + L.off);
     if (need_mask) {
@@ -195,7 +219,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-    mx = wave_max_halves(mx) * sl2;
+    mx = wave_max_halves(mx) * sc;
     if (__any(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
       // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
@@ -217,8 +241,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -msub));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, -msub));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sc, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
         lsum0 += p0;
         lsum1 += p1;
         pk[nb][r / 2] = pack2<T>(p0, p1);
@@ -262,7 +286,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
 }
 
 // fp32 I/O: one thread per query row, K/V tiles of 32 keys in LDS, fp32 FMA.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MOD>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   constexpr int BN = 32;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
@@ -314,6 +338,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) acc = fmaf(qv[dd], Ks[jj * D + dd], acc);
       const int key = k0 + jj;
+      if (MOD) {  // (bias - slope * |i + off - j|) * log2e; acc is already in log2 units
+        const float bval = (a.mod.bias != nullptr && my_q < a.s_q)
+                               ? bias1<Bf16T>((const char*)a.mod.bias +
+                                                  (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * 4,
+                                              1, key, a.s_kv)
+                               : 0.f;
+        const float slope = a.mod.slopes != nullptr ? a.mod.slopes[hq] : 0.f;
+        acc = fmaf(bval - slope * fabsf((float)(my_q + L.off - key)), kLog2e, acc);
+      }
       if (key >= L.lk || (CAUSAL && key > my_q + L.off)) acc = -INFINITY;
       s[jj] = acc;
       mx = fmaxf(mx, acc);
@@ -347,26 +380,40 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   }
 }
 
-template <typename T, int D, int NW>
-hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
+template <typename T, int D, int NW, bool MOD>
+hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
   const int bm = 32 * NW;
   const int n_qblk = (a.s_q + bm - 1) / bm;
   const dim3 grid(n_qblk * a.b * a.h_q), block(64 * NW);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW, MOD>), grid, block, 0, stream, a, n_qblk);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW, MOD>), grid, block, 0, stream, a, n_qblk);
   return hipGetLastError();
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
+  if (a.mod.slopes != nullptr || a.mod.bias != nullptr) return launch_mfma_dm<T, D, NW, true>(a, stream);
+  return launch_mfma_dm<T, D, NW, false>(a, stream);
 }
 
 template <int D>
 hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   const int n_qblk = (a.s_q + 63) / 64;
   const dim3 grid(n_qblk * a.b * a.h_q), block(64);
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, block, 0, stream, a, n_qblk);
-  else
-    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, block, 0, stream, a, n_qblk);
+  const bool mod = a.mod.slopes != nullptr || a.mod.bias != nullptr;
+  if (a.causal) {
+    if (mod)
+      hipLaunchKernelGGL((fwd_f32_kernel<D, true, true>), grid, block, 0, stream, a, n_qblk);
+    else
+      hipLaunchKernelGGL((fwd_f32_kernel<D, true, false>), grid, block, 0, stream, a, n_qblk);
+  } else {
+    if (mod)
+      hipLaunchKernelGGL((fwd_f32_kernel<D, false, true>), grid, block, 0, stream, a, n_qblk);
+    else
+      hipLaunchKernelGGL((fwd_f32_kernel<D, false, false>), grid, block, 0, stream, a, n_qblk);
+  }
   return hipGetLastError();
 }
 

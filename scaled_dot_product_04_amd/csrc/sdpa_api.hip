@@ -82,6 +82,33 @@ sdpa_status_t check_mask(sdpa_mask_t mask, const int32_t* seq_len_q, const int32
   return SDPA_OK;
 }
 
+// Validates the score modifiers and converts them; io is the input dtype.
+sdpa_status_t check_mod(const sdpa_score_mod_t* mod, sdpa_dtype_t io, sdpa::ScoreMod* out) {
+  *out = sdpa::ScoreMod{};
+  if (mod == nullptr || (mod->alibi_slopes == nullptr && mod->bias == nullptr)) return SDPA_OK;
+  if (io == SDPA_FP8_E4M3) return fail(SDPA_ERR_NOT_SUPPORTED, "score modifiers are not supported with fp8 inputs");
+  if (((uintptr_t)mod->alibi_slopes) % 4 != 0)
+    return fail(SDPA_ERR_NOT_SUPPORTED, "alibi_slopes must be 4-byte aligned");
+  out->slopes = mod->alibi_slopes;
+  if (mod->bias != nullptr) {
+    if (!(mod->bias_dtype == SDPA_F32 || (mod->bias_dtype == io && io != SDPA_F32)))
+      return fail(SDPA_ERR_NOT_SUPPORTED, "bias dtype %d must be F32 or the io dtype", (int)mod->bias_dtype);
+    const int eb = mod->bias_dtype == SDPA_F32 ? 4 : 2;
+    if (mod->bias_stride[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "bias s_kv stride must be 1");
+    if (((uintptr_t)mod->bias) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "bias is not 16-byte aligned");
+    for (int i = 0; i < 3; ++i)
+      if (mod->bias_stride[i] < 0 || (mod->bias_stride[i] * eb) % 16 != 0)
+        return fail(SDPA_ERR_NOT_SUPPORTED, "bias stride %d (%lld) must be >= 0 and a multiple of 16 bytes", i,
+                    (long long)mod->bias_stride[i]);
+    out->bias = mod->bias;
+    out->bias_f32 = eb == 4;
+    out->bb = mod->bias_stride[0];
+    out->bh = mod->bias_stride[1];
+    out->bs = mod->bias_stride[2];
+  }
+  return SDPA_OK;
+}
+
 sdpa_status_t check_sizes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
   if (b < 0 || s_q < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "b=%d and s_q=%d must be >= 0", b, s_q);
   if (h_q < 1 || h_kv < 1 || s_kv < 1 || d < 1)
@@ -132,7 +159,7 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
   g_last_error.clear();
   if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   return sdpa_fwd_ex(q, k, v, o, lse, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride,
-                     attn_scale, causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, in_dtype,
+                     attn_scale, causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, nullptr, in_dtype,
                      out_dtype, fp8, nullptr, 0, stream);
 }
 
@@ -147,9 +174,9 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
                           const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
                           float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
-                          const int32_t* seq_len_kv, sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
-                          const sdpa_fp8_scales_t* fp8, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          const int32_t* seq_len_kv, const sdpa_score_mod_t* mod, sdpa_dtype_t in_dtype,
+                          sdpa_dtype_t out_dtype, const sdpa_fp8_scales_t* fp8, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
@@ -185,10 +212,11 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   if (!ok)
     return fail(SDPA_ERR_NOT_SUPPORTED, "no forward kernel for in=%d out=%d d=%d", (int)in_dtype, (int)out_dtype, d);
 
+  sdpa::FwdArgs a{};
+  if ((st = check_mod(mod, in_dtype, &a.mod)) != SDPA_OK) return st;
   // Empty problem: nothing to compute or write; the (possibly NULL) pointers of
   // empty tensors are not inspected.
   if (b == 0 || s_q == 0) return SDPA_OK;
-  sdpa::FwdArgs a{};
   const int ein = elem_bytes(in_dtype), eout = elem_bytes(out_dtype);
   if ((st = check_tensor("q", q, q_stride, ein, &a.qs)) != SDPA_OK) return st;
   if ((st = check_tensor("k", k, k_stride, ein, &a.ks)) != SDPA_OK) return st;
@@ -224,7 +252,8 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   // Few query rows against many keys: the split-KV path, when its workspace
   // (if it needs one) is given; otherwise the row-block kernel.
   const sdpa::DecodePlan plan = sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io);
-  const bool split_kv = plan.use && (plan.ws_bytes == 0 || workspace != nullptr);
+  const bool has_mod = a.mod.slopes != nullptr || a.mod.bias != nullptr;
+  const bool split_kv = plan.use && !has_mod && (plan.ws_bytes == 0 || workspace != nullptr);
   if (split_kv && plan.ws_bytes > 0) {
     if (workspace_bytes < plan.ws_bytes)
       return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the split-KV forward needs %zu",
@@ -268,7 +297,7 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
   if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   return sdpa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride,
                      v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, attn_scale,
-                     causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, dtype, workspace,
+                     causal ? SDPA_MASK_CAUSAL : SDPA_MASK_NONE, nullptr, nullptr, nullptr, dtype, workspace,
                      workspace_bytes, stream);
 }
 
@@ -278,8 +307,8 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
                           const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
                           const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4],
                           float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
-                          const int32_t* seq_len_kv, sdpa_dtype_t dtype, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          const int32_t* seq_len_kv, const sdpa_score_mod_t* mod, sdpa_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
@@ -290,6 +319,7 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
   if (!((dtype == SDPA_BF16 || dtype == SDPA_F16) && (d == 64 || d == 128)))
     return fail(SDPA_ERR_NOT_SUPPORTED, "no backward kernel for dtype=%d d=%d", (int)dtype, d);
   sdpa::BwdArgs a{};
+  if ((st = check_mod(mod, dtype, &a.mod)) != SDPA_OK) return st;
   const int eb = elem_bytes(dtype);
   const sdpa::Io io = dtype == SDPA_BF16 ? sdpa::Io::BF16 : sdpa::Io::F16;
   if (b == 0) return SDPA_OK;  // empty problem: every tensor is empty

@@ -13,6 +13,15 @@ struct Strides3 {
   int64_t b, h, s;
 };
 
+// Score modifiers (additive bias tensor, ALiBi), added to the scaled scores
+// before the mask: S += bias[b][h][i][j] - slopes[h] * |i + off - j|.
+struct ScoreMod {
+  const float* slopes;  // device fp32 [h_q], or null
+  const void* bias;     // device bias (fp32, or 16-bit of the io type), or null
+  int bias_f32;         // 1: fp32 bias, 0: 16-bit
+  int64_t bb, bh, bs;   // element strides of the bias in (b, h, s_q); s_kv stride 1; 0 broadcasts
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -25,6 +34,7 @@ struct FwdArgs {
   int bottom_right;        // causal diagonal aligned to the end of the key range
   const int32_t* seq_q;    // device [b] valid query rows, or null (= s_q)
   const int32_t* seq_kv;   // device [b] valid keys, or null (= s_kv)
+  ScoreMod mod;            // bias / ALiBi (both null: none)
   float scale;  // attn_scale (already multiplied by the fp8 q/k descales for fp8)
   // fp8 only
   float descale_v, scale_p, descale_p;
@@ -46,6 +56,7 @@ struct BwdArgs {
   int bottom_right;
   const int32_t* seq_q;
   const int32_t* seq_kv;
+  ScoreMod mod;
   float scale;
   float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
 };

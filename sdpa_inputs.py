@@ -142,6 +142,14 @@ def make_lengths(b: int, s: int, seed: int, min_len: int = 0) -> torch.Tensor:
     return lens
 
 
+def make_bias(shape: tuple, seed: int, dtype: str = "f32") -> torch.Tensor:
+    """Additive score bias (b or 1, h or 1, s_q, s_kv): N(0, 1) from a CPU
+    generator seeded with ``seed``, rounded to ``dtype``."""
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x.to(_TORCH_DTYPES[dtype])
+
+
 def empty_logical(b: int, h: int, s: int, d: int, layout: str, dtype: str,
                   device="cpu") -> torch.Tensor:
     """Uninitialised (b, h, s, d) view in ``layout`` (for outputs and gradients)."""

@@ -137,7 +137,8 @@ def _fwd_ex(mask=1, lq=None, lk=None, **kw):
     S = ctypes.c_int64 * 4
     st = lib.sdpa_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 2, 64, 64, 128, S(*_bshd(2, 4, 64, 128)),
                          S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 2, 64, 128)), S(*_bshd(2, 4, 64, 128)), 0.088,
-                         mask, lq, lk, kw.get("tin", sdpa.SDPA_BF16), sdpa.SDPA_BF16, None, None, 0, None)
+                         mask, lq, lk, kw.get("mod"), kw.get("tin", sdpa.SDPA_BF16), sdpa.SDPA_BF16, None, None, 0,
+                         None)
     return st, lib.sdpa_last_error().decode()
 
 
@@ -147,6 +148,12 @@ def _fwd_ex(mask=1, lq=None, lk=None, **kw):
     (dict(lq=FAKE + 2), 2, "4-byte aligned"),
     (dict(lk=FAKE + 1), 2, "4-byte aligned"),
     (dict(mask=2, tin=9), 1, "dtype"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(FAKE + 2, None, 0, (0, 0, 0, 1)))), 2, "alibi_slopes must be 4-byte"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(None, FAKE, sdpa.SDPA_F16, (0, 0, 64, 1)))), 2, "bias dtype"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(None, FAKE, sdpa.SDPA_BF16, (0, 0, 64, 2)))), 1, "s_kv stride"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(None, FAKE + 4, sdpa.SDPA_F32, (0, 0, 64, 1)))), 2, "16-byte aligned"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(None, FAKE, sdpa.SDPA_BF16, (0, 0, 66, 1)))), 2, "multiple of 16"),
+    (dict(mod=ctypes.pointer(sdpa.ScoreMod(FAKE, None, 0, (0, 0, 0, 1))), tin=sdpa.SDPA_FP8_E4M3), 1, "fp8 scales"),
 ])
 def test_forward_ex_validation_errors(kw, status, needle):
     st, msg = _fwd_ex(**kw)
@@ -162,7 +169,7 @@ def test_backward_ex_validation_errors():
 
     def call(mask, lq):
         st = lib.sdpa_bwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, b, hq, hkv, s, s, d,
-                             qs, ks, ks, qs, qs, qs, ks, ks, 0.088, mask, lq, None, sdpa.SDPA_BF16, FAKE,
+                             qs, ks, ks, qs, qs, qs, ks, ks, 0.088, mask, lq, None, None, sdpa.SDPA_BF16, FAKE,
                              1 << 20, None)
         return st, lib.sdpa_last_error().decode()
 
