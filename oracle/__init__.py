@@ -10,7 +10,10 @@ from .sdpa_oracle import (  # noqa: F401
     attention_backward,
     attention_forward,
     attention_probs,
+    dropout_keep_threshold,
+    dropout_mask,
     fp8_dequantize,
     fp8_e4m3_decode,
+    philox4x32_10,
     sdpa_flops,
 )

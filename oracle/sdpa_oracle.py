@@ -135,7 +135,8 @@ def _bias_rows(bias, bi, hq, ridx, lk):
 def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                       causal: bool, heads=None, rows=None, row_block: int = _ROW_BLOCK,
                       seq_len_q=None, seq_len_kv=None, align: str = "top_left", bias=None,
-                      alibi_slopes=None):
+                      alibi_slopes=None, dropout_p: float = 0.0, dropout_seed: int = 0,
+                      dropout_offset: int = 0):
     """Forward pass O = softmax(scale * Q K^T + mask) V and LSE, in float64.
 
     Follows the JAX attention codelab's step 1 formula and step 4 dense form
@@ -151,6 +152,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     placement of the causal diagonal.
     bias: optional additive bias (b or 1, h_q or 1, s_q, s_kv); alibi_slopes:
     optional per-query-head ALiBi slopes (h_q,).
+    dropout_p, dropout_seed, dropout_offset: dropout of the attention weights,
+    O = (P * Z) V with Z from ``dropout_mask``; LSE is that of the undropped P.
     Returns (O, LSE): O has shape (b, h_q, n_rows, d) and LSE (b, h_q, n_rows);
     entries for heads not in ``heads`` are NaN. Rows that see no key have
     O = 0 and LSE = -inf.
@@ -173,6 +176,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
             slope = None if alibi_slopes is None else float(alibi_slopes[hq])
             s = _masked_scores(qr, ridx, kh, scale, causal, lq, lk, off, _bias_rows(bias, bi, hq, ridx, lk), slope)
             p, m, l = _softmax_rows(s)
+            if dropout_p > 0:
+                p = p * dropout_mask(bi * h_q + hq, ridx, lk, dropout_p, dropout_seed, dropout_offset)
             out[bi, hq, r0:r0 + len(ridx)] = p @ vh
             with np.errstate(divide="ignore"):  # ln 0 = -inf for rows that see no key
                 lse[bi, hq, r0:r0 + len(ridx)] = m + np.log(l)
@@ -204,7 +209,8 @@ def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                        scale: float, causal: bool, kv_heads=None, row_block: int = _ROW_BLOCK,
                        seq_len_q=None, seq_len_kv=None, align: str = "top_left", bias=None,
-                       alibi_slopes=None):
+                       alibi_slopes=None, dropout_p: float = 0.0, dropout_seed: int = 0,
+                       dropout_offset: int = 0):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for the forward above, in float64.
 
     The pages show only that a forward+backward SDPA exists (the cuDNN 9 blog,
@@ -225,6 +231,9 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
     seq_len_q, seq_len_kv, align: as in ``attention_forward``; rows that see
     no key have P = 0, hence dQ = 0 and no contribution to dK, dV.
     bias, alibi_slopes: as in ``attention_forward``; they only change P.
+    dropout_p, dropout_seed, dropout_offset: as in ``attention_forward``; with
+    Z the scaled mask, O = (P * Z) V, dV = (P * Z)^T dO, dP = (dO V^T) * Z and
+    dS = P * (dP - D), D_i = sum_d dO_id O_id (still equal to sum_j P_ij dP_ij).
     """
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
@@ -250,10 +259,12 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
                 slope = None if alibi_slopes is None else float(alibi_slopes[hq])
                 p, _, _ = _softmax_rows(_masked_scores(qr, ridx, kh, scale, causal, lq, lk, off,
                                                        _bias_rows(bias, bi, hq, ridx, lk), slope))
-                o = p @ vh
+                z = (dropout_mask(bi * h_q + hq, ridx, lk, dropout_p, dropout_seed, dropout_offset)
+                     if dropout_p > 0 else 1.0)
+                o = (p * z) @ vh
                 dvec = (dor * o).sum(axis=1)
-                dv_g[:lk] += p.T @ dor
-                dp = dor @ vh.T
+                dv_g[:lk] += (p * z).T @ dor
+                dp = (dor @ vh.T) * z
                 ds = p * (dp - dvec[:, None])
                 dq_h[ridx] = scale * (ds @ kh)
                 dk_g[:lk] += scale * (ds.T @ qr)
@@ -261,6 +272,61 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
         dk[bi, g] = dk_g
         dv[bi, g] = dv_g
     return dq, dk, dv
+
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers (Salmon et al. 2011, Philox4x32)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)  # key schedule increments (golden ratio, sqrt(3) - 1)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011), element-wise over uint32 arrays.
+
+    One round: (hi0, lo0) = M0 * c0 and (hi1, lo1) = M1 * c2 as 64-bit
+    products; the new counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the
+    key then advances by (W0, W1) modulo 2^32.
+    """
+    mask = np.uint64(0xFFFFFFFF)
+    c = [np.asarray(x, dtype=np.uint64) & mask for x in (c0, c1, c2, c3)]
+    k = [np.asarray(k0, dtype=np.uint64) & mask, np.asarray(k1, dtype=np.uint64) & mask]
+    for rnd in range(10):
+        if rnd > 0:
+            k = [(k[0] + np.uint64(_PHILOX_W[0])) & mask, (k[1] + np.uint64(_PHILOX_W[1])) & mask]
+        p0 = np.uint64(_PHILOX_M[0]) * c[0]
+        p1 = np.uint64(_PHILOX_M[1]) * c[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c = [hi1 ^ c[1] ^ k[0], lo1, hi0 ^ c[3] ^ k[1], lo0]
+    return tuple(x.astype(np.uint32) for x in c)
+
+
+def dropout_keep_threshold(p: float) -> int:
+    """k8 = round((1 - p) * 256): an element is kept iff its random byte < k8."""
+    return int(min(256, max(0, round((1.0 - float(p)) * 256.0))))
+
+
+def dropout_mask(bh: int, rows, n_keys: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Scaled dropout mask Z (len(rows) x n_keys) of query head slot bh = b * h_q + h.
+
+    Reading (the SDPA node's ``dropout`` option has no semantics on the pages):
+    element (i, j) takes byte (j mod 4) of word (i mod 4) of
+    Philox4x32-10(counter = (j // 4, i // 4, bh, offset), key = (seed mod 2^32,
+    seed // 2^32)); it is kept iff that byte < k8 = round((1 - p) 256), and a
+    kept element is scaled by 256 / k8 (so E[Z] = 1 exactly).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    k8 = dropout_keep_threshold(p)
+    if k8 == 0:
+        return np.zeros((len(rows), n_keys))
+    jj = np.arange(n_keys, dtype=np.int64)
+    c0 = np.broadcast_to(jj[None, :] >> 2, (len(rows), n_keys))
+    c1 = np.broadcast_to(rows[:, None] >> 2, (len(rows), n_keys))
+    words = philox4x32_10(c0, c1, np.full(c0.shape, bh), np.full(c0.shape, offset & 0xFFFFFFFF),
+                          seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    w = np.stack(words, axis=0).astype(np.uint64)           # 4 x rows x keys
+    sel = w[rows[:, None] % 4, np.arange(len(rows))[:, None], jj[None, :]]
+    byte = (sel >> (np.uint64(8) * (jj[None, :] % 4).astype(np.uint64))) & np.uint64(0xFF)
+    return np.where(byte < k8, 256.0 / k8, 0.0)
 
 
 def alibi_slopes(h: int) -> np.ndarray:
@@ -310,7 +376,8 @@ def sdpa_flops(b: int, h_q: int, s_q: int, s_kv: int, d: int, causal: bool) -> f
 
 
 __all__ = [
-    "attention_forward", "attention_backward", "attention_probs", "alibi_slopes",
+    "attention_forward", "attention_backward", "attention_probs", "alibi_slopes", "philox4x32_10",
+    "dropout_mask", "dropout_keep_threshold",
     "fp8_e4m3_decode", "fp8_dequantize", "sdpa_flops",
 ]
 
