@@ -112,14 +112,28 @@ typedef enum {
  *   bias_stride   element strides in (b, h, s_q, s_kv) order; the s_kv stride
  *                 must be 1; 0 broadcasts over b or h; the s_q stride must be a
  *                 multiple of 16 bytes' worth of elements.
- * Not supported with FP8 inputs (SDPA_ERR_NOT_SUPPORTED); the split-KV forward
- * path is not taken when modifiers are present.
+ * Not supported with FP8 inputs, and dropout not with F32 inputs
+ * (SDPA_ERR_NOT_SUPPORTED); the split-KV forward path is not taken when
+ * modifiers are present.
  */
 typedef struct {
   const float* alibi_slopes;
   const void* bias;
   sdpa_dtype_t bias_dtype;
   int64_t bias_stride[4];
+  /* Dropout of the attention weights (the node's `dropout` option; BF16 / F16
+   * only): O = (P * Z) V with P the softmax of the modified, masked scores and
+   * Z from a counter-based Philox4x32-10 stream (Salmon et al., SC 2011):
+   * element (i, j) of query-head slot b * h_q + h takes byte (j mod 4) of word
+   * (i mod 4) of Philox4x32-10(counter = (j / 4, i / 4, slot, dropout_offset),
+   * key = (seed mod 2^32, seed / 2^32)); it is kept iff the byte is below
+   * k8 = round((1 - dropout_p) * 256) (ties to even), and kept weights are
+   * scaled by 256 / k8. LSE is that of the undropped weights. The backward
+   * regenerates the same Z from the same three values. dropout_p in [0, 1];
+   * 0 disables. Advance dropout_offset between calls for a fresh mask. */
+  float dropout_p;
+  uint64_t dropout_seed;
+  uint32_t dropout_offset;
 } sdpa_score_mod_t;
 
 typedef struct {

@@ -40,7 +40,8 @@ class Fp8Scales(ctypes.Structure):
 class ScoreMod(ctypes.Structure):
     """sdpa_score_mod_t: optional ALiBi slopes and additive bias tensor."""
     _fields_ = [("alibi_slopes", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int),
-                ("bias_stride", ctypes.c_int64 * 4)]
+                ("bias_stride", ctypes.c_int64 * 4), ("dropout_p", ctypes.c_float),
+                ("dropout_seed", ctypes.c_uint64), ("dropout_offset", ctypes.c_uint32)]
 
 
 class SdpaError(RuntimeError):
@@ -148,12 +149,15 @@ def _lens(t, b, device, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, device):
+def _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, device, dropout=None):
     """Build the sdpa_score_mod_t for an optional bias tensor (b or 1, h_q or 1,
-    s_q, s_kv) and optional fp32 ALiBi slopes (h_q,), or None."""
-    if bias is None and alibi_slopes is None:
+    s_q, s_kv), optional fp32 ALiBi slopes (h_q,) and optional dropout
+    (p, seed, offset), or None."""
+    if bias is None and alibi_slopes is None and (dropout is None or dropout[0] == 0):
         return None
     m = ScoreMod()
+    if dropout is not None:
+        m.dropout_p, m.dropout_seed, m.dropout_offset = float(dropout[0]), int(dropout[1]), int(dropout[2])
     if alibi_slopes is not None:
         if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (h_q,) or \
                 not alibi_slopes.is_contiguous() or alibi_slopes.device != device:
@@ -192,7 +196,8 @@ def fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, dtype) -> int:
 
 def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: bool = True,
         fp8: Fp8Scales | None = None, out_dtype=None, seq_len_q=None, seq_len_kv=None, bias=None,
-        alibi_slopes=None, workspace=None, split_kv: bool = True, stream=None):
+        alibi_slopes=None, dropout_p: float = 0.0, dropout_seed: int = 0, dropout_offset: int = 0,
+        workspace=None, split_kv: bool = True, stream=None):
     """O (and LSE) of fused attention. Returns (out, lse); lse is None in inference mode.
 
     q: (b, h_q, s_q, d); k, v: (b, h_kv, s_kv, d); all on the GPU.
@@ -203,6 +208,8 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     mask); rows that see no key get O = 0 and LSE = -inf.
     bias, alibi_slopes: optional score modifiers added to the scaled scores
     (bias (b or 1, h_q or 1, s_q, s_kv), fp32 or q's dtype; slopes fp32 (h_q,)).
+    dropout_p, dropout_seed, dropout_offset: dropout of the attention weights
+    (Philox4x32-10 stream; the backward must get the same three values).
     workspace: device uint8 buffer for the split-KV path (few query rows,
     many keys); allocated here when the shape needs one and none is given,
     unless split_kv is False (then no workspace is passed, and shapes whose
@@ -214,7 +221,8 @@ def fwd(q, k, v, *, scale: float, causal=False, out=None, lse=None, return_lse: 
     in_code = _DTYPE_CODES[q.dtype]
     mask = _mask_code(causal)
     lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
-    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device)
+    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device,
+                     (dropout_p, dropout_seed, dropout_offset))
     if out_dtype is None:
         out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if out is None:
@@ -247,18 +255,20 @@ def bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, causal, dtype) -> int:
 
 
 def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, dv=None,
-        workspace=None, seq_len_q=None, seq_len_kv=None, bias=None, alibi_slopes=None, stream=None):
+        workspace=None, seq_len_q=None, seq_len_kv=None, bias=None, alibi_slopes=None,
+        dropout_p: float = 0.0, dropout_seed: int = 0, dropout_offset: int = 0, stream=None):
     """(dQ, dK, dV) of L = sum(O * dO). dK/dV are summed over each KV head's query group.
 
-    causal, seq_len_q, seq_len_kv, bias, alibi_slopes: those of the forward that
-    produced o and lse.
+    causal, seq_len_q, seq_len_kv, bias, alibi_slopes, dropout_*: those of the
+    forward that produced o and lse.
     """
     lib = load_library()
     b, h_q, s_q, d = q.shape
     h_kv, s_kv = k.shape[1], k.shape[2]
     mask = _mask_code(causal)
     lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
-    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device)
+    mod = _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, q.device,
+                     (dropout_p, dropout_seed, dropout_offset))
     dq = _like_q(q, q.dtype) if dq is None else dq
     dk = _like_q(k, k.dtype) if dk is None else dk
     dv = _like_q(v, v.dtype) if dv is None else dv

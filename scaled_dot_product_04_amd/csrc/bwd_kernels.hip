@@ -384,39 +384,44 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
       }
     }
-    // Score modifiers of this (query head, query row, key), log2 units.
-    float madd[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) madd[r] = 0.f;
-    if (MOD) {
-      const int hq = hq_base + it / nq;
-      const float slope2 = a.mod.slopes != nullptr ? a.mod.slopes[hq] * kLog2e : 0.f;
-      const char* bias_bh =
-          a.mod.bias != nullptr
-              ? (const char*)a.mod.bias + (bi * a.mod.bb + hq * a.mod.bh) * (a.mod.bias_f32 ? 4 : 2)
-              : nullptr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + acc_row(r, h);
-        const void* brow = (bias_bh != nullptr && qi < a.s_q)
-                               ? (const void*)(bias_bh + (int64_t)qi * a.mod.bs * (a.mod.bias_f32 ? 4 : 2))
-                               : nullptr;
-        madd[r] = fmaf(bias1<T>(brow, a.mod.bias_f32, my_key, a.s_kv), kLog2e,
-                       -slope2 * fabsf((float)(qi + L.off - my_key)));
-      }
-    }
+    // Score modifiers of this query head (log2 units), applied per row group below.
+    const int hq_it = hq_base + it / nq;
+    const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq_it] * kLog2e : 0.f;
+    const char* bias_bh = (MOD && a.mod.bias != nullptr)
+                              ? (const char*)a.mod.bias + (bi * a.mod.bb + hq_it * a.mod.bh) * (a.mod.bias_f32 ? 4 : 2)
+                              : nullptr;
     uint32_t ppk[8], dspk[8];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * h;
       const f32x4 l4 = *(const f32x4*)(&lse2s[row0]);
       const f32x4 d4 = *(const f32x4*)(&dels[row0]);
+      // Dropout words of queries q0 + row0 .. +3 (one per query) at this key.
+      const u32x4 dw = (MOD && a.mod.drop_k8 < 256)
+                           ? drop_words((uint32_t)my_key >> 2, (uint32_t)(q0 + row0) >> 2,
+                                        (uint32_t)(bi * a.h_q + hq_it), a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
+                           : u32x4{0u, 0u, 0u, 0u};
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, madd[4 * r4 + e] - l4[e]));
-        pv[e] = p;
-        dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
+        float madd = 0.f;
+        if (MOD) {
+          const int qi = q0 + row0 + e;
+          const void* brow = (bias_bh != nullptr && qi < a.s_q)
+                                 ? (const void*)(bias_bh + (int64_t)qi * a.mod.bs * (a.mod.bias_f32 ? 4 : 2))
+                                 : nullptr;
+          madd = fmaf(bias1<T>(brow, a.mod.bias_f32, my_key, a.s_kv), kLog2e,
+                      -slope2 * fabsf((float)(qi + L.off - my_key)));
+        }
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, madd - l4[e]));
+        if (MOD) {  // dV takes P Z (Z's scale applied at the end); dS = P (Z dP - D)
+          const bool keep = drop_keep(dw[e], my_key & 3, a.mod.drop_k8);
+          pv[e] = keep ? p : 0.f;
+          dsv[e] = p * ((keep ? a.mod.drop_scale * dp[4 * r4 + e] : 0.f) - d4[e]);
+        } else {
+          pv[e] = p;
+          dsv[e] = p * (dp[4 * r4 + e] - d4[e]);
+        }
       }
       ppk[2 * r4] = pack2<T>(pv[0], pv[1]);
       ppk[2 * r4 + 1] = pack2<T>(pv[2], pv[3]);
@@ -438,6 +443,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 
   if (my_key >= a.s_kv) return;
+  const float vsc = MOD ? a.mod.drop_scale : 1.f;  // dV = (P Z)^T dO, Z = keep * drop_scale
   if (n_split == 1) {
     uint16_t* dkp = (uint16_t*)a.dk + bi * a.dks.b + g * a.dks.h + (int64_t)my_key * a.dks.s;
     uint16_t* dvp = (uint16_t*)a.dv + bi * a.dvs.b + g * a.dvs.h + (int64_t)my_key * a.dvs.s;
@@ -449,8 +455,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         u32x2 wk, wv;
         wk.x = pack2<T>(dk[db][4 * rq] * a.scale, dk[db][4 * rq + 1] * a.scale);
         wk.y = pack2<T>(dk[db][4 * rq + 2] * a.scale, dk[db][4 * rq + 3] * a.scale);
-        wv.x = pack2<T>(dv[db][4 * rq], dv[db][4 * rq + 1]);
-        wv.y = pack2<T>(dv[db][4 * rq + 2], dv[db][4 * rq + 3]);
+        wv.x = pack2<T>(dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc);
+        wv.y = pack2<T>(dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc);
         *(u32x2*)(dkp + d0) = wk;
         *(u32x2*)(dvp + d0) = wv;
       }
@@ -467,7 +473,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         const int d0 = db * 32 + 8 * rq + 4 * h;
         *(f32x4*)(pk + d0) = f32x4{dk[db][4 * rq] * a.scale, dk[db][4 * rq + 1] * a.scale,
                                    dk[db][4 * rq + 2] * a.scale, dk[db][4 * rq + 3] * a.scale};
-        *(f32x4*)(pv + d0) = f32x4{dv[db][4 * rq], dv[db][4 * rq + 1], dv[db][4 * rq + 2], dv[db][4 * rq + 3]};
+        *(f32x4*)(pv + d0) =
+            f32x4{dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc, dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc};
       }
   }
 }
@@ -631,13 +638,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
     }
     uint32_t dspk[NSB][8];
 #pragma unroll
-    for (int nb = 0; nb < NSB; ++nb)
+    for (int nb = 0; nb < NSB; ++nb) {
+      uint32_t dw[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        dw[q4] = (MOD && a.mod.drop_k8 < 256)
+                     ? drop_word((uint32_t)(k0 + nb * 32 + 8 * q4 + 4 * h) >> 2, my_q, (uint32_t)(bi * a.h_q + hq),
+                                 a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
+                     : 0u;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, madd[nb][r] - lse2));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, madd[nb][r + 1] - lse2));
-        dspk[nb][r / 2] = pack2<T>(p0 * (dp[nb][r] - dl), p1 * (dp[nb][r + 1] - dl));
+        float z0 = 1.f, z1 = 1.f;  // dS = P (Z dP - D)
+        if (MOD) {
+          z0 = drop_keep(dw[r / 4], r % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
+          z1 = drop_keep(dw[r / 4], (r + 1) % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
+        }
+        dspk[nb][r / 2] = pack2<T>(p0 * (z0 * dp[nb][r] - dl), p1 * (z1 * dp[nb][r + 1] - dl));
       }
+    }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int t2 = 0; t2 < kKTile / 16; ++t2) {
@@ -737,7 +757,7 @@ hipError_t launch_bwd_m(const BwdArgs& a, Io io, hipStream_t stream, const Timin
 }
 
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
-  if (a.mod.slopes != nullptr || a.mod.bias != nullptr) return launch_bwd_m<true>(a, io, stream, te);
+  if (has_mod(a.mod)) return launch_bwd_m<true>(a, io, stream, te);
   return launch_bwd_m<false>(a, io, stream, te);
 }
 

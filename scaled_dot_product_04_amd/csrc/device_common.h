@@ -235,4 +235,45 @@ __device__ __forceinline__ float bias1(const void* bias_row, int bias_f32, int k
   return bias_f32 ? ((const float*)bias_row)[key] : to_f32<T>(((const uint16_t*)bias_row)[key]);
 }
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): per round, (hi0, lo0) = M0 * c0 and
+// (hi1, lo1) = M1 * c2 as 64-bit products, the counter becomes
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0), and the key advances by (W0, W1).
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c2 = hi0 ^ c3 ^ k1;
+    c1 = lo1;
+    c3 = lo0;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Word (row % 4) of the dropout stream block (row / 4, key / 4): its byte
+// (key % 4) decides element (row, key) (see ScoreMod).
+__device__ __forceinline__ uint32_t drop_word(uint32_t key4, int row, uint32_t slot, uint32_t offset,
+                                              uint32_t seed_lo, uint32_t seed_hi) {
+  const u32x4 w = philox4x32_10(key4, (uint32_t)row >> 2, slot, offset, seed_lo, seed_hi);
+  const int m = row & 3;
+  return m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w;
+}
+
+// The four words of the block (rows row4*4 .. +3, keys key4*4 .. +3).
+__device__ __forceinline__ u32x4 drop_words(uint32_t key4, uint32_t row4, uint32_t slot, uint32_t offset,
+                                            uint32_t seed_lo, uint32_t seed_hi) {
+  return philox4x32_10(key4, row4, slot, offset, seed_lo, seed_hi);
+}
+
+__device__ __forceinline__ bool drop_keep(uint32_t word, int byte, int k8) {
+  return (int)((word >> (8 * byte)) & 0xFFu) < k8;
+}
+
 }  // namespace sdpa

@@ -55,9 +55,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   constexpr int NT = 64 * NW;    // threads
   constexpr int BM = 32 * NW;    // query rows per workgroup
   // Keys per K/V tile: 128 at d = 128 (halves the per-tile barrier, row-max
-  // reduction and loop overhead; 244 VGPRs, 135 KB LDS at 8 waves), 64 at
-  // d = 64 (keeps three waves per SIMD).
-  constexpr int kBN = D == 128 ? 128 : 64;
+  // reduction and loop overhead; 246 VGPRs, 135 KB LDS at 8 waves), 64 at
+  // d = 64 (keeps three waves per SIMD) and with score modifiers (their
+  // registers would not fit beside 128-key score tiles).
+  constexpr int kBN = (D == 128 && !MOD) ? 128 : 64;
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // computed, so the row max and the exponent use them as they are.
   const float sc = MOD ? 1.f : sl2;
   const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
+  const uint32_t drop_slot = (uint32_t)(bi * a.h_q + hq);
   const void* bias_row =
       (MOD && a.mod.bias != nullptr && my_q < a.s_q)
           ? (const void*)((const char*)a.mod.bias +
@@ -243,9 +245,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sc, -msub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
-        lsum0 += p0;
+        lsum0 += p0;  // the row sum uses the undropped weights
         lsum1 += p1;
-        pk[nb][r / 2] = pack2<T>(p0, p1);
+        if (MOD) {
+          // Dropout word of this row for the 4-key group of r (0, i.e. every
+          // byte kept, without dropout).
+          const uint32_t dw = (a.mod.drop_k8 < 256)
+                                  ? drop_word((uint32_t)(k0 + nb * 32 + 8 * (r / 4) + 4 * h) >> 2, my_q, drop_slot,
+                                              a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
+                                  : 0u;
+          const bool k_0 = drop_keep(dw, r % 4, a.mod.drop_k8);
+          const bool k_1 = drop_keep(dw, (r + 1) % 4, a.mod.drop_k8);
+          pk[nb][r / 2] = pack2<T>(k_0 ? p0 : 0.f, k_1 ? p1 : 0.f);
+        } else {
+          pk[nb][r / 2] = pack2<T>(p0, p1);
+        }
       }
     l_run += lsum0 + lsum1;
 
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // no key, get O = 0 and LSE = -inf.
   const float l_tot = wave_sum_halves(l_run);
   const bool live = my_q < L.lq && l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
+  const float inv = live ? (MOD ? a.mod.drop_scale : 1.f) / l_tot : 0.f;
   if (my_q < a.s_q) {
     E* op = (E*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
@@ -394,7 +408,7 @@ hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int NW>
 hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
-  if (a.mod.slopes != nullptr || a.mod.bias != nullptr) return launch_mfma_dm<T, D, NW, true>(a, stream);
+  if (has_mod(a.mod)) return launch_mfma_dm<T, D, NW, true>(a, stream);
   return launch_mfma_dm<T, D, NW, false>(a, stream);
 }
 
@@ -402,7 +416,7 @@ template <int D>
 hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   const int n_qblk = (a.s_q + 63) / 64;
   const dim3 grid(n_qblk * a.b * a.h_q), block(64);
-  const bool mod = a.mod.slopes != nullptr || a.mod.bias != nullptr;
+  const bool mod = has_mod(a.mod);
   if (a.causal) {
     if (mod)
       hipLaunchKernelGGL((fwd_f32_kernel<D, true, true>), grid, block, 0, stream, a, n_qblk);

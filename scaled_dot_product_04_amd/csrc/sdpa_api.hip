@@ -85,7 +85,12 @@ sdpa_status_t check_mask(sdpa_mask_t mask, const int32_t* seq_len_q, const int32
 // Validates the score modifiers and converts them; io is the input dtype.
 sdpa_status_t check_mod(const sdpa_score_mod_t* mod, sdpa_dtype_t io, sdpa::ScoreMod* out) {
   *out = sdpa::ScoreMod{};
-  if (mod == nullptr || (mod->alibi_slopes == nullptr && mod->bias == nullptr)) return SDPA_OK;
+  out->drop_k8 = 256;  // no dropout
+  out->drop_scale = 1.f;
+  if (mod == nullptr) return SDPA_OK;
+  if (!(mod->dropout_p >= 0.f && mod->dropout_p <= 1.f))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "dropout_p must be in [0, 1]");
+  if (mod->alibi_slopes == nullptr && mod->bias == nullptr && mod->dropout_p == 0.f) return SDPA_OK;
   if (io == SDPA_FP8_E4M3) return fail(SDPA_ERR_NOT_SUPPORTED, "score modifiers are not supported with fp8 inputs");
   if (((uintptr_t)mod->alibi_slopes) % 4 != 0)
     return fail(SDPA_ERR_NOT_SUPPORTED, "alibi_slopes must be 4-byte aligned");
@@ -105,6 +110,16 @@ sdpa_status_t check_mod(const sdpa_score_mod_t* mod, sdpa_dtype_t io, sdpa::Scor
     out->bb = mod->bias_stride[0];
     out->bh = mod->bias_stride[1];
     out->bs = mod->bias_stride[2];
+  }
+  if (mod->dropout_p > 0.f) {
+    if (io != SDPA_BF16 && io != SDPA_F16)
+      return fail(SDPA_ERR_NOT_SUPPORTED, "dropout needs BF16 or F16 inputs");
+    // keep iff random byte < k8 = round((1 - p) * 256), ties to even; kept weights scale by 256 / k8
+    out->drop_k8 = (int)nearbyint((1.0 - (double)mod->dropout_p) * 256.0);
+    out->drop_scale = out->drop_k8 > 0 ? (float)(256.0 / out->drop_k8) : 0.f;
+    out->seed_lo = (uint32_t)(mod->dropout_seed & 0xFFFFFFFFu);
+    out->seed_hi = (uint32_t)(mod->dropout_seed >> 32);
+    out->offset = mod->dropout_offset;
   }
   return SDPA_OK;
 }
@@ -252,8 +267,7 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   // Few query rows against many keys: the split-KV path, when its workspace
   // (if it needs one) is given; otherwise the row-block kernel.
   const sdpa::DecodePlan plan = sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io);
-  const bool has_mod = a.mod.slopes != nullptr || a.mod.bias != nullptr;
-  const bool split_kv = plan.use && !has_mod && (plan.ws_bytes == 0 || workspace != nullptr);
+  const bool split_kv = plan.use && !sdpa::has_mod(a.mod) && (plan.ws_bytes == 0 || workspace != nullptr);
   if (split_kv && plan.ws_bytes > 0) {
     if (workspace_bytes < plan.ws_bytes)
       return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the split-KV forward needs %zu",

@@ -20,7 +20,17 @@ struct ScoreMod {
   const void* bias;     // device bias (fp32, or 16-bit of the io type), or null
   int bias_f32;         // 1: fp32 bias, 0: 16-bit
   int64_t bb, bh, bs;   // element strides of the bias in (b, h, s_q); s_kv stride 1; 0 broadcasts
+  // Dropout of the attention weights: element (i, j) of query-head slot
+  // b * h_q + h is kept iff byte (j % 4) of word (i % 4) of
+  // Philox4x32-10(counter (j / 4, i / 4, slot, offset), key (seed_lo, seed_hi))
+  // is below drop_k8; kept weights are scaled by drop_scale = 256 / drop_k8.
+  int drop_k8;          // 256: no dropout
+  float drop_scale;
+  uint32_t seed_lo, seed_hi, offset;
 };
+
+// Whether any modifier is active (the kernels take their MOD variant).
+inline bool has_mod(const ScoreMod& m) { return m.slopes != nullptr || m.bias != nullptr || m.drop_k8 < 256; }
 
 struct FwdArgs {
   const void* q;

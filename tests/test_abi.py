@@ -193,3 +193,10 @@ def test_forward_workspace_size_selects_split_kv_shapes():
     assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_FP8_E4M3) == 0
     assert f(1, 6, 4, 1, 8192, 128, sdpa.SDPA_BF16) == 0
     assert f(1, 32, 8, 1, 8192, 128, sdpa.SDPA_BF16) % 16 == 0
+
+
+def test_dropout_probability_validated():
+    st, msg = _fwd_ex(mod=ctypes.pointer(sdpa.ScoreMod(None, None, 0, (0, 0, 0, 1), 1.5, 0, 0)))
+    assert st == 1 and "dropout_p" in msg
+    st, msg = _fwd_ex(mod=ctypes.pointer(sdpa.ScoreMod(None, None, 0, (0, 0, 0, 1), float("nan"), 0, 0)))
+    assert st == 1 and "dropout_p" in msg
