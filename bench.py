@@ -125,8 +125,9 @@ def write_traffic_record(kernel: str, fetch_db: str, write_db: str, copy_fetch_d
     import json
     import sqlite3
 
-    short = {"bwd_dkdv": "bwd_dkdv_kernel<sdpa::Bf16T, 128, true>", "fwd": "fwd_mfma_kernel<sdpa::Bf16T, 128, true, 8>",
-             "bwd_dq": "bwd_dq_kernel<sdpa::Bf16T, 128, true>"}[kernel]
+    short = {"bwd_dkdv": "bwd_dkdv_kernel<sdpa::Bf16T, 128, true, false>",
+             "fwd": "fwd_mfma_kernel<sdpa::Bf16T, 128, true, 8, false>",
+             "bwd_dq": "bwd_dq_kernel<sdpa::Bf16T, 128, true, false>"}[kernel]
 
     def per_dispatch(db, counter, name_part=None):
         c = sqlite3.connect(db)
@@ -267,6 +268,7 @@ def main() -> int:
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the extra KV-cache decode measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the extra padding-mask (ragged batch) measurement")
+    ap.add_argument("--no-mods", action="store_true", help="skip the extra score-modifier (ALiBi, dropout) measurement")
     ap.add_argument("--traffic-record", nargs=5, metavar=("KERNEL", "FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
                                                           "COPY_WRITE_DB"),
                     help="write the HBM-traffic record of KERNEL from rocprofv3 --pmc result databases and exit "
@@ -278,9 +280,9 @@ def main() -> int:
     if args.traffic_record:
         k, f_db, w_db, cf_db, cw_db = args.traffic_record
         cmds = [f"rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
-                f"--no-fp8 --no-decode --no-varlen",
+                f"--no-fp8 --no-decode --no-varlen --no-mods",
                 f"rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
-                f"--no-fp8 --no-decode --no-varlen",
+                f"--no-fp8 --no-decode --no-varlen --no-mods",
                 "rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
                 "rocprofv3 --pmc WRITE_SIZE -d <out> -o run -- python3 bench.py --copy-reference",
                 f"python3 bench.py --traffic-record {k} <fetch db> <write db> <copy fetch db> <copy write db>"]
@@ -377,6 +379,32 @@ def main() -> int:
     log(f"[bench] fwd {fwd_tflops:.1f} TFLOP/s ({100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% peak); "
         f"bwd {bwd_tflops:.1f}; fwd+bwd {value:.1f} ({100 * value / PEAK_BF16_TFLOPS:.1f}%)")
 
+    mods = None
+    if not args.no_mods:
+        # The same workload and tensors with score modifiers: ALiBi, then
+        # dropout p = 0.1 (counted flops unchanged; the modifiers are VALU work).
+        mods = {}
+        slopes = sdpa.alibi_slopes(w.h_q, device="cuda:0")
+        for name, kw in (("alibi", {"alibi_slopes": slopes}),
+                         ("dropout_0.1", {"dropout_p": 0.1, "dropout_seed": 1234, "dropout_offset": 0})):
+            def mstep(kw=kw):
+                sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, stream=stream, **kw)
+                sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv,
+                         workspace=ws, stream=stream, **kw)
+            for _ in range(args.warmup):
+                mstep()
+            a0, a1 = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            hip.record(a0, sh)
+            for _ in range(args.steps):
+                mstep()
+            hip.record(a1, sh)
+            torch.cuda.synchronize()
+            mms = hip.ms(a0, a1) / args.steps
+            mods[name] = {"ms_per_step": round(mms, 4), "tflops": round(step_flops / (mms / 1e3) / 1e12, 2),
+                          "vs_plain": round(ms_step / mms, 3)}
+        log(f"[bench] score modifiers (same step): {mods}")
+
     fp8 = None
     if not args.no_fp8:
         fp8 = fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
@@ -424,6 +452,7 @@ def main() -> int:
         "fp8_forward": fp8,
         "decode_forward": dec,
         "varlen_forward_backward": vl,
+        "score_modifiers": mods,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
