@@ -364,8 +364,30 @@ def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return sign * val
 
 
-def fp8_dequantize(codes: np.ndarray, descale: float) -> np.ndarray:
-    """Real values x = e4m3(code) * descale that an fp8 kernel receives."""
+def fp8_e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP e5m2 codes (uint8) as float64: the gradient format of the
+    HYBRID FP8 recipe (JAX attention codelab, step 10: E4M3 in the forward,
+    E5M2 in the backward).
+
+    Layout s eeeee mm, exponent bias 15 (IEEE-like). e = 0: subnormal
+    (m / 4) * 2^-14; e = 31: infinity (m = 0) or NaN; every other code is
+    (1 + m / 4) * 2^(e - 15). Largest finite value 57344.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    normal = (1.0 + m / 4.0) * np.power(2.0, e - 15.0)
+    sub = (m / 4.0) * 2.0 ** -14
+    val = np.where(e == 0, sub, normal)
+    val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def fp8_dequantize(codes: np.ndarray, descale: float, fmt: str = "e4m3") -> np.ndarray:
+    """Real values x = fp8(code) * descale that an fp8 kernel receives (fmt e4m3 or e5m2)."""
+    if fmt == "e5m2":
+        return fp8_e5m2_decode(codes) * float(descale)
     return fp8_e4m3_decode(codes) * float(descale)
 
 
@@ -378,7 +400,7 @@ def sdpa_flops(b: int, h_q: int, s_q: int, s_kv: int, d: int, causal: bool) -> f
 __all__ = [
     "attention_forward", "attention_backward", "attention_probs", "alibi_slopes", "philox4x32_10",
     "dropout_mask", "dropout_keep_threshold",
-    "fp8_e4m3_decode", "fp8_dequantize", "sdpa_flops",
+    "fp8_e4m3_decode", "fp8_e5m2_decode", "fp8_dequantize", "sdpa_flops",
 ]
 
 if __name__ == "__main__":  # pragma: no cover - tiny self-demo

@@ -26,6 +26,7 @@ from dataclasses import dataclass, field
 import torch
 
 FP8_MAX = 448.0  # largest finite OCP e4m3fn value
+FP8_E5M2_MAX = 57344.0  # largest finite OCP e5m2 value
 
 _TORCH_DTYPES = {
     "f32": torch.float32,
@@ -69,17 +70,19 @@ def randn_logical(gen: torch.Generator, b: int, h: int, s: int, d: int,
     return as_logical(phys, layout)
 
 
-def quantize_fp8(x: torch.Tensor) -> tuple[torch.Tensor, float]:
-    """Per-tensor fp8-e4m3 quantisation: returns (e4m3 tensor of x's shape/layout, descale).
+def quantize_fp8(x: torch.Tensor, fmt: str = "e4m3") -> tuple[torch.Tensor, float]:
+    """Per-tensor fp8 quantisation: returns (fp8 tensor of x's shape/layout, descale).
 
-    scale = 448 / amax(x); x8 = e4m3(clamp(x * scale)); descale = 1 / scale (fp32).
+    scale = fmax / amax(x) (fmax 448 for e4m3, 57344 for e5m2);
+    x8 = fp8(clamp(x * scale)); descale = 1 / scale (fp32).
     """
+    fmax, tdt = (FP8_E5M2_MAX, torch.float8_e5m2) if fmt == "e5m2" else (FP8_MAX, torch.float8_e4m3fn)
     amax = float(x.abs().max())
     if amax == 0.0:
         amax = 1.0
-    scale = FP8_MAX / amax
-    scaled = (x.float() * scale).clamp_(-FP8_MAX, FP8_MAX)
-    return scaled.to(torch.float8_e4m3fn), float(torch.tensor(1.0 / scale, dtype=torch.float32))
+    scale = fmax / amax
+    scaled = (x.float() * scale).clamp_(-fmax, fmax)
+    return scaled.to(tdt), float(torch.tensor(1.0 / scale, dtype=torch.float32))
 
 
 @dataclass
@@ -128,7 +131,11 @@ def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
         out["scale_p"] = FP8_MAX
         out["descale_p"] = 1.0 / FP8_MAX
     if with_grad if with_grad is not None else w.backward:
-        out["do"] = randn_logical(gen, w.b, w.h_q, w.s_q, w.d, w.layout, w.out_dtype)
+        if w.dtype == "fp8":  # HYBRID: the gradient in e5m2
+            do32 = randn_logical(gen, w.b, w.h_q, w.s_q, w.d, w.layout, "f32")
+            out["do"], out["descale_do"] = quantize_fp8(do32, "e5m2")
+        else:
+            out["do"] = randn_logical(gen, w.b, w.h_q, w.s_q, w.d, w.layout, w.out_dtype)
     return out
 
 
@@ -193,6 +200,13 @@ def hd128(s: int) -> Workload:
 def gqa(h_kv: int) -> Workload:
     return Workload(f"gqa_hkv{h_kv}", 2, 32, h_kv, 4096, 4096, 128, "bf16", "bf16", True,
                     1.0 / math.sqrt(128), "bshd", 42 + h_kv, backward=True)
+
+
+def fp8_hd128() -> Workload:
+    """The hd128 causal training shape with fp8 tensors (e4m3) and an e5m2
+    gradient, the HYBRID recipe of the JAX attention codelab (step 10)."""
+    return Workload("fp8_hd128_causal_s8192", 2, 16, 16, 8192, 8192, 128, "fp8", "bf16", True,
+                    1.0 / math.sqrt(128), "bshd", 9128, backward=True)
 
 
 def fp8() -> Workload:

@@ -18,7 +18,7 @@ import torch
 
 import sdpa_inputs
 from oracle import (attention_backward, attention_forward, attention_probs,
-                    fp8_dequantize, fp8_e4m3_decode)
+                    fp8_dequantize, fp8_e4m3_decode, fp8_e5m2_decode)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_printed_values.json")
 
@@ -270,6 +270,44 @@ def test_fp8_decode_matches_torch_for_all_codes():
     assert fp8_e4m3_decode(np.array([0x7E]))[0] == 448.0
     assert fp8_e4m3_decode(np.array([0x38]))[0] == 1.0
     assert fp8_e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_fp8_e5m2_decode_matches_torch_for_all_codes():
+    """E5M2 (the HYBRID format's gradient type, codelab step 10) against torch's
+    float8_e5m2 for every code, plus the values the format's definition fixes."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = fp8_e5m2_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 6  # exponent 31 with a nonzero mantissa, both signs
+    assert (np.isnan(ours) == nan).all()
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    assert fp8_e5m2_decode(np.array([0x7B]))[0] == 57344.0
+    assert fp8_e5m2_decode(np.array([0x3C]))[0] == 1.0
+    assert fp8_e5m2_decode(np.array([0x01]))[0] == 2.0 ** -16
+    assert fp8_e5m2_decode(np.array([0x7C]))[0] == np.inf
+    assert fp8_e5m2_decode(np.array([0xFC]))[0] == -np.inf
+    # e5m2 is the upper byte of an IEEE half: same value for every code
+    half = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(ours[~nan], half[~nan])
+    assert fp8_dequantize(np.array([0x3C], dtype=np.uint8), 0.25, "e5m2")[0] == 0.25
+
+
+def test_fp8_e5m2_gradient_roundtrip():
+    """dO of an fp8 backward workload is e5m2 with its descale; it dequantises to
+    within e5m2's half-ulp (relative 2^-3) of the drawn values."""
+    w = sdpa_inputs.Workload("t", 1, 2, 2, 64, 64, 32, "fp8", "bf16", False, 0.2, "bshd", 5, backward=True)
+    ins = sdpa_inputs.make_inputs(w)
+    assert ins["do"].dtype == torch.float8_e5m2
+    deq = fp8_dequantize(ins["do"].view(torch.uint8).numpy(), ins["descale_do"], "e5m2")
+    gen = torch.Generator().manual_seed(5)
+    for _ in range(3):
+        sdpa_inputs.randn_logical(gen, 1, 2, 64, 32, "bshd", "f32")
+    do32 = sdpa_inputs.randn_logical(gen, 1, 2, 64, 32, "bshd", "f32").numpy()
+    amax = np.abs(do32).max()
+    assert np.abs(deq).max() == pytest.approx(amax, rel=1e-6)
+    big = np.abs(do32) > amax * 2 ** -10
+    assert (np.abs(deq - do32)[big] <= np.abs(do32)[big] * 2 ** -3 * 1.0001).all()
 
 
 def test_fp8_inputs_roundtrip():
