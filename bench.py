@@ -185,6 +185,51 @@ def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: i
             "pct_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
 
 
+def fp8_hd128_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int,
+                               bf16_ms_step: float) -> dict:
+    """Extra measurement (not part of `value`): the hd128 causal training step
+    (b2 h16 s8192 d128) with e4m3 tensors and an e5m2 gradient (HYBRID):
+    fp8 forward, then the fp8 backward (widening + 16-bit kernels); TFLOP/s
+    of the same counted flops as the bf16 step, and the speed-up over it."""
+    w = sdpa_inputs.fp8_hd128()
+    ins = sdpa_inputs.make_inputs(w)
+    dev = torch.device("cuda:0")
+    g = {k: sdpa_inputs.to_device_like(v, dev) for k, v in ins.items() if isinstance(v, torch.Tensor)}
+    sc = sdpa.Fp8Scales(ins["descale_q"], ins["descale_k"], ins["descale_v"], ins["scale_p"], ins["descale_p"])
+    o = sdpa._like_q(g["q"], torch.bfloat16)
+    lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+    dq = sdpa._like_q(g["q"], torch.bfloat16)
+    dk, dv = sdpa._like_q(g["k"], torch.bfloat16), sdpa._like_q(g["v"], torch.bfloat16)
+    ws = torch.empty(max(16, sdpa.bwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, True,
+                                                     torch.float8_e4m3fn)), dtype=torch.uint8, device=dev)
+    bw = dict(scale=w.scale, causal=True, descale_q=ins["descale_q"], descale_k=ins["descale_k"],
+              descale_v=ins["descale_v"], descale_do=ins["descale_do"], dq=dq, dk=dk, dv=dv, workspace=ws,
+              stream=stream)
+
+    def fwd():
+        sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, fp8=sc, stream=stream)
+
+    def bwd():
+        sdpa.bwd_fp8(g["q"], g["k"], g["v"], o, g["do"], lse, **bw)
+
+    res = {"workload": w.name, "b": w.b, "h": w.h_q, "s": w.s_q, "d": w.d, "formats": "e4m3 q/k/v, e5m2 dO"}
+    for name, fn in (("forward", fwd), ("backward", bwd), ("step", lambda: (fwd(), bwd()))):
+        for _ in range(warmup):
+            fn()
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, sh)
+        for _ in range(steps):
+            fn()
+        hip.record(b, sh)
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / steps
+        fl = {"forward": 1.0, "backward": 2.5, "step": 3.5}[name] * w.fwd_flops
+        res[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms / 1e3) / 1e12, 2)}
+    res["step_speedup_vs_bf16"] = round(bf16_ms_step / res["step"]["ms"], 3)
+    return res
+
+
 def decode_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
     """Extra measurement (not part of `value`): a KV-cache step (b8, h_q 32 /
     h_kv 8, one query row, 32768 keys, d128 bf16), bound by HBM: the K/V bytes
@@ -405,10 +450,13 @@ def main() -> int:
                           "vs_plain": round(ms_step / mms, 3)}
         log(f"[bench] score modifiers (same step): {mods}")
 
-    fp8 = None
+    fp8 = fp8_train = None
     if not args.no_fp8:
         fp8 = fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps)
         log(f"[bench] fp8 forward (b4 h8 s8192 d256, non-causal): {fp8}")
+        fp8_train = fp8_hd128_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, args.warmup, args.steps,
+                                               ms_step)
+        log(f"[bench] fp8 hd128 causal forward + backward: {fp8_train}")
 
     dec = None
     if not args.no_decode:
@@ -450,6 +498,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "fp8_forward": fp8,
+        "fp8_hd128_forward_backward": fp8_train,
         "decode_forward": dec,
         "varlen_forward_backward": vl,
         "score_modifiers": mods,

@@ -62,7 +62,8 @@ typedef enum {
   SDPA_F32 = 0,
   SDPA_F16 = 1,
   SDPA_BF16 = 2,
-  SDPA_FP8_E4M3 = 3 /* OCP e4m3fn: 4 exponent bits, 3 mantissa bits, max 448, no inf */
+  SDPA_FP8_E4M3 = 3, /* OCP e4m3fn: 4 exponent bits, 3 mantissa bits, max 448, no inf */
+  SDPA_FP8_E5M2 = 4  /* OCP e5m2: 5 exponent bits, 2 mantissa bits, max 57344, inf (gradients) */
 } sdpa_dtype_t;
 
 typedef enum {
@@ -220,7 +221,9 @@ size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
 
 /*
  * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned
- * use). 0 is a valid answer only for empty problems.
+ * use). 0 is a valid answer only for empty problems. With dtype
+ * SDPA_FP8_E4M3 it is the size sdpa_bwd_fp8 needs (larger: it adds the bf16
+ * copies of q, k, v and dout).
  */
 size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d,
                                int causal, sdpa_dtype_t dtype);
@@ -273,6 +276,50 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
                           sdpa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Per-tensor descale factors of the fp8 backward's inputs: real value =
+ * fp8 code * descale (all finite and > 0). */
+typedef struct {
+  float descale_q;
+  float descale_k;
+  float descale_v;
+  float descale_do;
+} sdpa_fp8_bwd_scales_t;
+
+/*
+ * FP8 backward: dQ, dK, dV of L = sum(O * dO) for the fp8 forward, in the
+ * HYBRID format of the JAX attention codelab (step 10): tensors in e4m3 for
+ * the forward pass, the gradient dO in e5m2 for the backward pass, each with a
+ * per-tensor scale (the recipe's delayed scaling tracks those factors; they
+ * arrive here as descale = 1 / scale).
+ *
+ *   q, k, v     e4m3 codes, [b, h, s, d] with strides as in sdpa_fwd (the
+ *               forward's inputs); values q * descale_q etc.
+ *   o           the fp8 forward's BF16 output; lse its fp32 LSE (required).
+ *   dout        dO codes in do_dtype (SDPA_FP8_E5M2, or SDPA_FP8_E4M3),
+ *               value dout * descale_do.
+ *   dq, dk, dv  BF16 gradients with respect to the real-valued q, k, v.
+ *   mask, seq_len_q, seq_len_kv  as in sdpa_bwd_ex (those of the forward).
+ *   workspace   at least sdpa_bwd_workspace_size(..., SDPA_FP8_E4M3) bytes,
+ *               16-byte aligned; scratch.
+ * Supported: d in {64, 128}; no score modifiers. The codes are widened
+ * exactly to bf16 in the workspace (both formats embed in bf16) and the 16-bit
+ * backward kernels run on them with the descale factors folded into the
+ * softmax scale and the output scales, so the result is that of the BF16
+ * backward on the dequantised tensors, up to rounding order.
+ */
+sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                           const int64_t q_stride[4], const int64_t k_stride[4],
+                           const int64_t v_stride[4], const int64_t o_stride[4],
+                           const int64_t do_stride[4], const int64_t dq_stride[4],
+                           const int64_t dk_stride[4], const int64_t dv_stride[4],
+                           float attn_scale, sdpa_mask_t mask,
+                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                           sdpa_dtype_t do_dtype, const sdpa_fp8_bwd_scales_t* scales,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Timing hook (diagnostics only; GPU-time-only reporting as in the cuDNN 9
  * blog's "SDPA performance" section). Registers `n` caller-created HIP events
@@ -281,7 +328,8 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
  *   sdpa_fwd: events[0] before its kernel, events[1] after it (n >= 2);
  *   sdpa_bwd: events[0] before the D = rowsum(dO * O) kernel, events[1] after
  *             it, events[2] after the dK/dV kernel (and its split reduction),
- *             events[3] after the dQ kernel (n >= 4).
+ *             events[3] after the dQ kernel (n >= 4); sdpa_bwd_fp8 records
+ *             the same four after its widening kernels.
  * The library does not own the events. Returns SDPA_ERR_INVALID_ARGUMENT for
  * n < 0, n > 8, or events == NULL with n > 0.
  */

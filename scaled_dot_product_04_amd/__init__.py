@@ -19,13 +19,13 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
-SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_FP8_E4M3 = 0, 1, 2, 3
+SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_FP8_E4M3, SDPA_FP8_E5M2 = 0, 1, 2, 3, 4
 SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_INVALID_ARGUMENT", 2: "SDPA_ERR_NOT_SUPPORTED",
                 3: "SDPA_ERR_WORKSPACE_TOO_SMALL", 4: "SDPA_ERR_HIP"}
 
 _DTYPE_CODES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16,
-                torch.float8_e4m3fn: SDPA_FP8_E4M3}
+                torch.float8_e4m3fn: SDPA_FP8_E4M3, torch.float8_e5m2: SDPA_FP8_E5M2}
 
 _Strides = ctypes.c_int64 * 4
 
@@ -35,6 +35,12 @@ class Fp8Scales(ctypes.Structure):
     _fields_ = [("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
                 ("descale_v", ctypes.c_float), ("scale_p", ctypes.c_float),
                 ("descale_p", ctypes.c_float)]
+
+
+class Fp8BwdScales(ctypes.Structure):
+    """sdpa_fp8_bwd_scales_t: descale factors of the fp8 backward's q, k, v and dO."""
+    _fields_ = [("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
+                ("descale_v", ctypes.c_float), ("descale_do", ctypes.c_float)]
 
 
 class ScoreMod(ctypes.Structure):
@@ -87,6 +93,10 @@ def load_library() -> ctypes.CDLL:
     lib.sdpa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                 i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, vp, vp,
                                 ctypes.POINTER(ScoreMod), i, vp, ctypes.c_size_t, vp]
+    lib.sdpa_bwd_fp8.restype = ctypes.c_int
+    lib.sdpa_bwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                 i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p, f, i, vp, vp,
+                                 i, ctypes.POINTER(Fp8BwdScales), vp, ctypes.c_size_t, vp]
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -287,6 +297,36 @@ def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, 
     return dq, dk, dv
 
 
-__all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_workspace_size", "alibi_slopes", "ScoreMod", "load_library", "library_path", "Fp8Scales",
+def bwd_fp8(q, k, v, o, dout, lse, *, scale: float, descale_q: float, descale_k: float,
+            descale_v: float, descale_do: float, causal=False, dq=None, dk=None, dv=None,
+            workspace=None, seq_len_q=None, seq_len_kv=None, stream=None):
+    """(dQ, dK, dV) in bf16 for the fp8 forward: q, k, v e4m3, dout e5m2 (or e4m3),
+    o the forward's bf16 output, lse its LSE; real values are code * descale.
+
+    causal, seq_len_q, seq_len_kv: those of the forward that produced o and lse.
+    """
+    lib = load_library()
+    b, h_q, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    mask = _mask_code(causal)
+    lq, lk = _lens(seq_len_q, b, q.device, "seq_len_q"), _lens(seq_len_kv, b, q.device, "seq_len_kv")
+    if dout.dtype not in (torch.float8_e5m2, torch.float8_e4m3fn):
+        raise TypeError(f"dout must be float8_e5m2 or float8_e4m3fn, got {dout.dtype}")
+    dq = _like_q(q, torch.bfloat16) if dq is None else dq
+    dk = _like_q(k, torch.bfloat16) if dk is None else dk
+    dv = _like_q(v, torch.bfloat16) if dv is None else dv
+    if workspace is None:
+        n = bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, mask != SDPA_MASK_NONE, torch.float8_e4m3fn)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    sc = Fp8BwdScales(float(descale_q), float(descale_k), float(descale_v), float(descale_do))
+    _check(lib.sdpa_bwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                            _ptr(dv), b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v),
+                            _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv),
+                            float(scale), mask, lq, lk, _DTYPE_CODES[dout.dtype], ctypes.byref(sc),
+                            _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+__all__ = ["fwd", "bwd", "bwd_fp8", "Fp8BwdScales", "SDPA_FP8_E5M2", "bwd_workspace_size", "fwd_workspace_size", "alibi_slopes", "ScoreMod", "load_library", "library_path", "Fp8Scales",
            "SdpaError", "SDPA_F32", "SDPA_F16", "SDPA_BF16", "SDPA_FP8_E4M3", "SDPA_MASK_NONE",
            "SDPA_MASK_CAUSAL", "SDPA_MASK_CAUSAL_BOTTOM_RIGHT"]

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (r < total && part == 0) a.delta[r] = acc;
+  if (r < total && part == 0) a.delta[r] = acc * a.delta_scale;
 }
 
 // Writes zeros to dK and dV (problems with no query rows).
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 
   if (my_key >= a.s_kv) return;
-  const float vsc = MOD ? a.mod.drop_scale : 1.f;  // dV = (P Z)^T dO, Z = keep * drop_scale
+  const float vsc = MOD ? a.dv_scale * a.mod.drop_scale : a.dv_scale;  // dV = (P Z)^T dO, Z = keep * drop_scale
   if (n_split == 1) {
     uint16_t* dkp = (uint16_t*)a.dk + bi * a.dks.b + g * a.dks.h + (int64_t)my_key * a.dks.s;
     uint16_t* dvp = (uint16_t*)a.dv + bi * a.dvs.b + g * a.dvs.h + (int64_t)my_key * a.dvs.s;
@@ -453,8 +453,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = db * 32 + 8 * rq + 4 * h;
         u32x2 wk, wv;
-        wk.x = pack2<T>(dk[db][4 * rq] * a.scale, dk[db][4 * rq + 1] * a.scale);
-        wk.y = pack2<T>(dk[db][4 * rq + 2] * a.scale, dk[db][4 * rq + 3] * a.scale);
+        wk.x = pack2<T>(dk[db][4 * rq] * a.dk_scale, dk[db][4 * rq + 1] * a.dk_scale);
+        wk.y = pack2<T>(dk[db][4 * rq + 2] * a.dk_scale, dk[db][4 * rq + 3] * a.dk_scale);
         wv.x = pack2<T>(dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc);
         wv.y = pack2<T>(dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc);
         *(u32x2*)(dkp + d0) = wk;
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = db * 32 + 8 * rq + 4 * h;
-        *(f32x4*)(pk + d0) = f32x4{dk[db][4 * rq] * a.scale, dk[db][4 * rq + 1] * a.scale,
-                                   dk[db][4 * rq + 2] * a.scale, dk[db][4 * rq + 3] * a.scale};
+        *(f32x4*)(pk + d0) = f32x4{dk[db][4 * rq] * a.dk_scale, dk[db][4 * rq + 1] * a.dk_scale,
+                                   dk[db][4 * rq + 2] * a.dk_scale, dk[db][4 * rq + 3] * a.dk_scale};
         *(f32x4*)(pv + d0) =
             f32x4{dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc, dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc};
       }
@@ -679,8 +679,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = db * 32 + 8 * rq + 4 * h;
         u32x2 w;
-        w.x = pack2<T>(dq[db][4 * rq] * a.scale, dq[db][4 * rq + 1] * a.scale);
-        w.y = pack2<T>(dq[db][4 * rq + 2] * a.scale, dq[db][4 * rq + 3] * a.scale);
+        w.x = pack2<T>(dq[db][4 * rq] * a.dq_scale, dq[db][4 * rq + 1] * a.dq_scale);
+        w.y = pack2<T>(dq[db][4 * rq + 2] * a.dq_scale, dq[db][4 * rq + 3] * a.dq_scale);
         *(u32x2*)(dqp + d0) = w;
       }
   }

@@ -47,12 +47,21 @@ int elem_bytes(sdpa_dtype_t t) {
     case SDPA_F32: return 4;
     case SDPA_F16:
     case SDPA_BF16: return 2;
-    case SDPA_FP8_E4M3: return 1;
+    case SDPA_FP8_E4M3:
+    case SDPA_FP8_E5M2: return 1;
   }
   return 0;
 }
 
-bool valid_dtype(int t) { return t >= SDPA_F32 && t <= SDPA_FP8_E4M3; }
+bool valid_dtype(int t) { return t >= SDPA_F32 && t <= SDPA_FP8_E5M2; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bytes of the fp8 backward's bf16 copies of q, dout (b*h_q*s_q*d each) and
+// k, v (b*h_kv*s_kv*d each), placed after the 16-bit backward's workspace.
+size_t fp8_stage_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
+  return 2 * align256((size_t)b * h_q * s_q * d * 2) + 2 * align256((size_t)b * h_kv * s_kv * d * 2);
+}
 
 // Checks one tensor's pointer and strides. Returns SDPA_OK or an error.
 sdpa_status_t check_tensor(const char* name, const void* p, const int64_t* st, int eb,
@@ -295,9 +304,10 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
 size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d, int causal,
                                sdpa_dtype_t dtype) {
   (void)causal;
-  (void)dtype;
   if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_kv <= 0 || d <= 0) return 0;
-  return sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  const size_t base = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  if (dtype == SDPA_FP8_E4M3) return align256(base) + fp8_stage_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  return base;
 }
 
 sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -380,6 +390,10 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
   a.seq_q = seq_len_q;
   a.seq_kv = seq_len_kv;
   a.scale = attn_scale;
+  a.dq_scale = attn_scale;
+  a.dk_scale = attn_scale;
+  a.dv_scale = 1.f;
+  a.delta_scale = 1.f;
   const size_t need = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
   if (workspace_bytes < need)
     return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -390,6 +404,120 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
     fprintf(stderr, "[sdpa] bwd io=%d d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d lens=%d\n", (int)io, d, b,
             h_q, h_kv, s_q, s_kv, (int)mask, (seq_len_q != nullptr) + 2 * (seq_len_kv != nullptr));
   return hip_status(sdpa::launch_bwd(a, io, stream, g_timing), "backward launch");
+}
+
+// The fp8 backward (JAX attention codelab, step 10, HYBRID format). With
+// codes Qc, Kc, Vc, dOc and descales sq, sk, sv, so (real X = Xc * sX):
+//   S     = attn_scale * sq * sk * Qc Kc^T          (softmax scale)
+//   dP    = so * sv * dOc Vc^T,  D = so * rowsum(dOc * O)
+//   dS    = P * (dP - D) = so * sv * P * (dOc Vc^T - D / (so * sv))
+// so the 16-bit kernels run on the widened codes with
+//   delta_scale = 1 / sv, dS' = P * (dOc Vc^T - rowsum(dOc * O) / sv),
+//   dQ = attn_scale * dS K   = (attn_scale * so * sv * sk) * dS' Kc,
+//   dK = attn_scale * dS^T Q = (attn_scale * so * sv * sq) * dS'^T Qc,
+//   dV = P^T dO              = so * P^T dOc.
+sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int b, int h_q, int h_kv, int s_q,
+                           int s_kv, int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                           const int64_t v_stride[4], const int64_t o_stride[4], const int64_t do_stride[4],
+                           const int64_t dq_stride[4], const int64_t dk_stride[4], const int64_t dv_stride[4],
+                           float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                           sdpa_dtype_t do_dtype, const sdpa_fp8_bwd_scales_t* scales, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  sdpa_status_t st;
+  if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
+  if ((st = check_mask(mask, seq_len_q, seq_len_kv)) != SDPA_OK) return st;
+  if (!(attn_scale > 0.f) || !isfinite(attn_scale))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
+  if (do_dtype != SDPA_FP8_E5M2 && do_dtype != SDPA_FP8_E4M3)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "do_dtype must be FP8_E5M2 or FP8_E4M3 (got %d)", (int)do_dtype);
+  if (scales == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 descale factors are NULL");
+  const float sq = scales->descale_q, sk = scales->descale_k, sv = scales->descale_v, so = scales->descale_do;
+  for (float x : {sq, sk, sv, so})
+    if (!(x > 0.f) || !isfinite(x)) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 descale factors must be finite and > 0");
+  if (!(d == 64 || d == 128)) return fail(SDPA_ERR_NOT_SUPPORTED, "no fp8 backward for d=%d", d);
+  sdpa::BwdArgs a{};
+  a.mod.drop_k8 = 256;  // no score modifiers
+  a.mod.drop_scale = 1.f;
+  if (b == 0) return SDPA_OK;
+  if (s_q == 0) {
+    if ((st = check_tensor("dk", dk, dk_stride, 2, &a.dks)) != SDPA_OK) return st;
+    if ((st = check_tensor("dv", dv, dv_stride, 2, &a.dvs)) != SDPA_OK) return st;
+    a.dk = dk;
+    a.dv = dv;
+    a.b = b;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.s_kv = s_kv;
+    a.d = d;
+    return hip_status(sdpa::launch_zero_dkdv(a, sdpa::Io::BF16, stream), "zero dK/dV launch");
+  }
+  if (lse == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse is required by the backward");
+  sdpa::Strides3 qs8, ks8, vs8, dos8;
+  if ((st = check_tensor("q", q, q_stride, 1, &qs8)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, 1, &ks8)) != SDPA_OK) return st;
+  if ((st = check_tensor("v", v, v_stride, 1, &vs8)) != SDPA_OK) return st;
+  if ((st = check_tensor("dout", dout, do_stride, 1, &dos8)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, 2, &a.os)) != SDPA_OK) return st;
+  if ((st = check_tensor("dq", dq, dq_stride, 2, &a.dqs)) != SDPA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_stride, 2, &a.dks)) != SDPA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_stride, 2, &a.dvs)) != SDPA_OK) return st;
+  if (((uintptr_t)lse) % 4 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "lse is not 4-byte aligned");
+  const size_t base = align256(sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d));
+  const size_t need = base + fp8_stage_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  if (workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (workspace == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)workspace) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "workspace is not 16-byte aligned");
+  // Workspace: [16-bit backward's scratch][q16][do16][k16][v16], compact [b][h][s][d] bf16.
+  char* w = (char*)workspace;
+  const size_t qbytes = align256((size_t)b * h_q * s_q * d * 2), kbytes = align256((size_t)b * h_kv * s_kv * d * 2);
+  void* q16 = w + base;
+  void* do16 = w + base + qbytes;
+  void* k16 = w + base + 2 * qbytes;
+  void* v16 = w + base + 2 * qbytes + kbytes;
+  const sdpa::Strides3 cq{(int64_t)h_q * s_q * d, (int64_t)s_q * d, d};
+  const sdpa::Strides3 ck{(int64_t)h_kv * s_kv * d, (int64_t)s_kv * d, d};
+  hipError_t e;
+  if ((e = sdpa::launch_fp8_widen(q, qs8, b, h_q, s_q, d, false, q16, stream)) != hipSuccess ||
+      (e = sdpa::launch_fp8_widen(dout, dos8, b, h_q, s_q, d, do_dtype == SDPA_FP8_E5M2, do16, stream)) != hipSuccess ||
+      (e = sdpa::launch_fp8_widen(k, ks8, b, h_kv, s_kv, d, false, k16, stream)) != hipSuccess ||
+      (e = sdpa::launch_fp8_widen(v, vs8, b, h_kv, s_kv, d, false, v16, stream)) != hipSuccess)
+    return hip_status(e, "fp8 widening launch");
+  a.q = q16;
+  a.k = k16;
+  a.v = v16;
+  a.o = o;
+  a.dout = do16;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.qs = cq;
+  a.dos = cq;
+  a.ks = ck;
+  a.vs = ck;
+  a.b = b;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.s_q = s_q;
+  a.s_kv = s_kv;
+  a.d = d;
+  a.causal = mask != SDPA_MASK_NONE;
+  a.bottom_right = mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT;
+  a.seq_q = seq_len_q;
+  a.seq_kv = seq_len_kv;
+  a.scale = attn_scale * sq * sk;
+  a.dq_scale = attn_scale * so * sv * sk;
+  a.dk_scale = attn_scale * so * sv * sq;
+  a.dv_scale = so;
+  a.delta_scale = 1.f / sv;
+  a.delta = (float*)workspace;
+  if (log_level() >= 2)
+    fprintf(stderr, "[sdpa] bwd_fp8 d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d do=%d\n", d, b, h_q, h_kv, s_q,
+            s_kv, (int)mask, (int)do_dtype);
+  return hip_status(sdpa::launch_bwd(a, sdpa::Io::BF16, stream, g_timing), "fp8 backward launch");
 }
 
 }  // extern "C"

@@ -67,7 +67,11 @@ struct BwdArgs {
   const int32_t* seq_q;
   const int32_t* seq_kv;
   ScoreMod mod;
-  float scale;
+  float scale;        // multiplies Q K^T inside the softmax
+  float dq_scale;     // dQ = dq_scale * dS K      (scale for real-valued inputs)
+  float dk_scale;     // dK = dk_scale * dS^T Q    (scale)
+  float dv_scale;     // dV = dv_scale * P^T dO    (1)
+  float delta_scale;  // D_i = delta_scale * sum_d dO_id * O_id (1)
   float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
 };
 
@@ -103,6 +107,10 @@ DecodePlan plan_decode(int b, int h_q, int h_kv, int s_q, int s_kv, int d, Io io
 hipError_t launch_fwd_decode(const FwdArgs& a, const DecodePlan& p, void* workspace, Io io, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te);
 hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
+// Exact widening of fp8 codes (e5m2 when e5m2, else e4m3) of a strided
+// [b][h][s][d] tensor into a compact bf16 [b][h][s][d] copy at dst.
+hipError_t launch_fp8_widen(const void* src, const Strides3& st, int b, int h, int s, int d, bool e5m2,
+                            void* dst, hipStream_t stream);
 
 // Workspace bytes the backward needs (see sdpa_bwd_workspace_size).
 size_t bwd_workspace_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d);

@@ -39,6 +39,8 @@ def f64(x: torch.Tensor, descale: float | None = None) -> np.ndarray:
     """Exact float64 values of a CPU tensor (fp8 codes times their descale)."""
     if x.dtype == torch.float8_e4m3fn:
         return fp8_dequantize(x.contiguous().view(torch.uint8).numpy(), descale)
+    if x.dtype == torch.float8_e5m2:
+        return fp8_dequantize(x.contiguous().view(torch.uint8).numpy(), descale, "e5m2")
     return x.double().numpy()
 
 
@@ -59,9 +61,9 @@ def oracle_fwd(w, ins, heads=None, rows=None):
     return attention_forward(q, k, v, w.scale, w.causal, heads=heads, rows=rows)
 
 
-def oracle_bwd(w, ins, kv_heads=None):
-    q, k, v, do = (f64(ins[n]) for n in ("q", "k", "v", "do"))
-    return attention_backward(q, k, v, do, w.scale, w.causal, kv_heads=kv_heads)
+def oracle_bwd(w, ins, kv_heads=None, **kw):
+    q, k, v, do = (f64(ins[n], ins.get("descale_" + n)) for n in ("q", "k", "v", "do"))
+    return attention_backward(q, k, v, do, w.scale, w.causal, kv_heads=kv_heads, **kw)
 
 
 def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:

@@ -200,3 +200,49 @@ def test_dropout_probability_validated():
     assert st == 1 and "dropout_p" in msg
     st, msg = _fwd_ex(mod=ctypes.pointer(sdpa.ScoreMod(None, None, 0, (0, 0, 0, 1), float("nan"), 0, 0)))
     assert st == 1 and "dropout_p" in msg
+
+
+def _bwd_fp8(**kw):
+    lib = sdpa.load_library()
+    b, hq, hkv, s, d = 2, 4, 2, 64, 128
+    a = dict(q=FAKE, do=FAKE, b=b, d=d, mask=1, do_dtype=sdpa.SDPA_FP8_E5M2,
+             scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.01, 0.01, 1e-4)), ws_bytes=1 << 30, qs8=None)
+    a.update(kw)
+    S = ctypes.c_int64 * 4
+    q16, k16 = S(*_bshd(b, hq, s, d)), S(*_bshd(b, hkv, s, d))
+    q8 = S(*(a["qs8"] or _bshd(b, hq, s, d)))
+    st = lib.sdpa_bwd_fp8(a["q"], FAKE, FAKE, FAKE, a["do"], FAKE, FAKE, FAKE, FAKE, a["b"], hq, hkv, s, s,
+                          a["d"], q8, k16, k16, q16, q16, q16, k16, k16, 0.088, a["mask"], None, None,
+                          a["do_dtype"], a["scales"], FAKE, a["ws_bytes"], None)
+    return st, lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(do=None), 1, "dout is NULL"),
+    (dict(mask=4), 1, "mask must be"),
+    (dict(do_dtype=sdpa.SDPA_BF16), 1, "do_dtype"),
+    (dict(scales=None), 1, "NULL"),
+    (dict(scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.0, 0.01, 1e-4))), 1, "finite and > 0"),
+    (dict(scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.01, float("inf"), 1e-4))), 1, "finite and > 0"),
+    (dict(d=256), 2, "no fp8 backward"),
+    (dict(ws_bytes=16), 3, "workspace"),
+    # an fp8 row of 128 codes with a 136-byte stride is not 16-byte aligned
+    (dict(qs8=(64 * 4 * 136, 136, 4 * 136, 1)), 2, "multiple of 16 bytes"),
+])
+def test_backward_fp8_validation_errors(kw, status, needle):
+    st, msg = _bwd_fp8(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_fp8_backward_workspace_holds_bf16_copies():
+    f = sdpa.load_library().sdpa_bwd_workspace_size
+    b, hq, hkv, s, d = 2, 16, 4, 1024, 128
+    plain = f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_BF16)
+    fp8 = f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_FP8_E4M3)
+    # q and dO (b*h_q*s*d each) and k, v (b*h_kv*s*d each) as bf16
+    assert fp8 >= plain + 2 * 2 * b * s * d * (hq + hkv)
+    assert fp8 % 16 == 0
+    st, msg = _fwd_ex(tin=sdpa.SDPA_FP8_E5M2)  # e5m2 is a gradient format only
+    assert st == 2 and "no forward kernel" in msg
