@@ -14,17 +14,18 @@
 //
 // Kernels (all atomic-free and deterministic):
 //  1. delta:  D = rowsum(dO * O) in fp32 (memory-bound).
-//  2. dK/dV:  KV-stationary. A workgroup owns 128 keys (32 per wave, held in
-//     registers); it loops over the query heads of its group and over 32-row
-//     query tiles, which are staged in LDS both row-major and transposed.
+//  2. dK/dV:  KV-stationary. A workgroup owns 256 keys (32 per wave) whose K
+//     and V rows stay in LDS; it loops over the query heads of its group and
+//     over 32-row query tiles staged row-major in LDS, read both as row
+//     operands and, through ds_read_b64_tr_b16, as transposed ones.
 //     Each lane owns one key column of S = Q K^T, so P and dS are directly the
 //     B operands of dV^T += dO^T P and dK^T += Q^T dS.
 //     When a GQA/MQA group would leave the GPU underfilled, the group's query
 //     heads are split over several workgroups that write fp32 partials.
 //  3. reduce: sums the partials of the splits in a fixed order.
 //  4. dQ:     Q-stationary, laid out like the forward: each lane owns one
-//     query column of S^T = K Q^T; dQ^T += K^T dS^T with K^T read from a
-//     transposed LDS copy of the K tile.
+//     query column of S^T = K Q^T; dQ^T += K^T dS^T with K^T read from the
+//     row-major K tile through ds_read_b64_tr_b16.
 #include "device_common.h"
 #include "sdpa_internal.h"
 
@@ -83,115 +84,6 @@ __global__ __launch_bounds__(256) void zero_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// A tile of R rows x D 16-bit elements in flight in registers, as 4x4
-// blocks (row group rg, column group dg). Each 16-lane group covers 4 column
-// groups x 4 row groups, so the transposed LDS writes of a group fall in
-// distinct banks and each row segment read from HBM is 128 B (d = 128).
-// Loads are raw buffer loads from a per-tile descriptor; rows past the end of
-// the tensor read as zero. Byte offsets inside a tile are loop-invariant.
-// From registers the tile is written to LDS row-major (row stride D + 8)
-// and/or transposed (row stride R + 4, one row per column of the tile).
-template <int R, int D>
-struct BlockTile {
-  static constexpr int DG = D / 4;
-  static constexpr int TOTAL = (R / 4) * DG;
-  static constexpr int NB = (TOTAL + 255) / 256;
-  static constexpr int RS = D + 8, TS = R + 4;
-  static_assert(DG % 4 == 0 && (R / 4) % 4 == 0, "block map needs 4x4 groups");
-  u32x2 v[NB][4];
-  uint32_t off[NB];   // byte offset of the block's first row
-  uint32_t rm_dst[NB], tr_dst[NB];
-  int64_t stride;
-
-  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
-    stride = row_stride;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = tid + 256 * i;
-      const int sub = c & 15, grp = c >> 4;
-      const int dg = (sub & 3) + 4 * (grp % (DG / 4));
-      const int rg = (sub >> 2) + 4 * (grp / (DG / 4));
-      off[i] = (uint32_t)((4 * rg) * row_stride * 2 + 8 * dg);
-      rm_dst[i] = (4 * rg) * RS + 4 * dg;
-      tr_dst[i] = (4 * dg) * TS + 4 * rg;
-    }
-  }
-  __device__ __forceinline__ bool active(int i, int tid) const { return TOTAL % 256 == 0 || tid + 256 * i < TOTAL; }
-  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows, int tid) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
-    const uint32_t rstep = (uint32_t)(stride * 2);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (!active(i, tid)) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[i][r] = buf_load8(rs, off[i] + r * rstep);
-    }
-  }
-  __device__ __forceinline__ void store_rm(uint16_t* rm, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (!active(i, tid)) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x2*)(&rm[rm_dst[i] + r * RS]) = v[i][r];
-    }
-  }
-  __device__ __forceinline__ void store_tr(uint16_t* tr, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (!active(i, tid)) continue;
-      u32x2 cols[4];
-      transpose4x4_b16(v[i], cols);
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) *(u32x2*)(&tr[tr_dst[i] + c2 * TS]) = cols[c2];
-    }
-  }
-};
-
-// A tile of R rows x D 16-bit elements in flight as 16-byte row chunks,
-// written to LDS row-major (row stride D + 8). Buffer loads as above.
-template <int R, int D>
-struct ChunkTile {
-  static constexpr int CH = D / 8;
-  static constexpr int NC = R * CH / 256;
-  static constexpr int RS = D + 8;
-  static_assert(NC * 256 == R * CH, "tile / thread mismatch");
-  u32x4 v[NC];
-  uint32_t off[NC], dst[NC];
-  int64_t stride;
-
-  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
-    stride = row_stride;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CH, cc = c % CH;
-      off[i] = (uint32_t)(r * row_stride * 2 + cc * 16);
-      dst[i] = r * RS + cc * 8;
-    }
-  }
-  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows, int tid) {
-    (void)tid;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
-#pragma unroll
-    for (int i = 0; i < NC; ++i) v[i] = buf_load16(rs, off[i]);
-  }
-  __device__ __forceinline__ void store(uint16_t* rm, int tid) const {
-    (void)tid;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) *(u32x4*)(&rm[dst[i]]) = v[i];
-  }
-};
-
-// A operand taken from a transposed LDS tile (row = feature index f, stride TS):
-// lane half h element m stands for row key_of(t, h, m) of the original tile.
-template <typename V8>
-__device__ __forceinline__ V8 read_tr_operand(const uint16_t* tr, int TS, int f, int t, int h) {
-  const uint16_t* p = tr + f * TS + 16 * t + 4 * h;
-  const u32x2 lo = *(const u32x2*)(p);
-  const u32x2 hi = *(const u32x2*)(p + 8);
-  return __builtin_bit_cast(V8, u32x4{lo.x, lo.y, hi.x, hi.y});
-}
-
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
@@ -236,6 +128,40 @@ struct TrLaneB {
   }
 };
 
+// A tile of R rows x D 16-bit elements in flight as 16-byte row chunks
+// (NT threads), written to LDS row-major in the bswz layout. Buffer loads;
+// rows past the end of the tensor read as zero.
+template <int R, int D, int NT>
+struct BswzTile {
+  static constexpr int CH = D / 8;
+  static constexpr int NC = R * CH / NT;
+  static_assert(NC * NT == R * CH, "tile / thread mismatch");
+  u32x4 v[NC];
+  uint32_t off[NC];
+  int dst[NC];
+  int64_t stride;
+
+  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
+    stride = row_stride;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = tid + NT * i;
+      const int r = c / CH, cc = c % CH;
+      off[i] = (uint32_t)(r * row_stride * 2 + cc * 16);
+      dst[i] = r * D + ((cc ^ bswz<D>(r)) * 8);
+    }
+  }
+  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) v[i] = buf_load16(rs, off[i]);
+  }
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) *(u32x4*)(&tile[dst[i]]) = v[i];
+  }
+};
+
 // KV-stationary dK/dV. A workgroup has 8 waves (two per SIMD) and 256 keys;
 // wave w owns keys 32 w .. 32 w + 31 of the block and accumulates their dK^T,
 // dV^T in VGPRs. The block's K and V rows sit in LDS for the whole kernel
@@ -253,7 +179,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int KVC = kKvBlock * CH / NT;     // K (and V) block chunks per thread
   constexpr int QCH = kQTile * CH;            // chunks of one Q (or dO) tile
-  static_assert(KVC * NT == kKvBlock * CH && QCH <= NT, "tile / thread mismatch");
+  constexpr int QPT = (QCH + NT - 1) / NT;    // of which each thread stages up to QPT
+  static_assert(KVC * NT == kKvBlock * CH, "tile / thread mismatch");
   __shared__ __attribute__((aligned(16))) uint16_t Kb[kKvBlock * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vb[kKvBlock * D];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kQTile * D];
@@ -322,23 +249,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   TrLaneB<D> trl;
   trl.init(lane);
 
-  // Q / dO tile staging: thread tid < QCH owns chunk (r, cc) of each tile.
-  const bool stager = tid < QCH;
-  const int sr = tid / CH, scc = tid % CH;
-  const uint32_t qoff = (uint32_t)(sr * a.qs.s * 2 + scc * 16);
-  const uint32_t doff = (uint32_t)(sr * a.dos.s * 2 + scc * 16);
-  const int sdst = sr * D + ((scc ^ bswz<D>(sr)) * 8);
-  u32x4 qreg = u32x4{0, 0, 0, 0}, dreg = u32x4{0, 0, 0, 0};
+  // Q / dO tile staging: chunk c = tid + NT i (c < QCH) is row c / CH, column
+  // chunk c % CH. (When every thread stages, no branch guards the loads: the
+  // unconditional form schedules measurably better.)
+  uint32_t qoff[QPT], doff[QPT];
+  int sdst[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int c = tid + NT * i, sr = c / CH, scc = c % CH;
+    qoff[i] = (uint32_t)(sr * a.qs.s * 2 + scc * 16);
+    doff[i] = (uint32_t)(sr * a.dos.s * 2 + scc * 16);
+    sdst[i] = sr * D + ((scc ^ bswz<D>(sr)) * 8);
+  }
+  u32x4 qreg[QPT], dreg[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) qreg[i] = dreg[i] = u32x4{0, 0, 0, 0};
   float lreg = 0.f, creg = 0.f;
   auto load_tile = [&](int it) {
     const int hq = hq_base + it / nq;
     const int q0 = (qt0 + it % nq) * kQTile;
     const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h + (int64_t)q0 * a.qs.s;
     const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)q0 * a.dos.s;
-    if (stager) {  // rows at or past lq read as zero
-      qreg = buf_load16(make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2)), qoff);
-      dreg = buf_load16(make_rsrc(dop, tile_bytes(q0, L.lq, a.dos.s, D, 2)), doff);
-    }
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2));
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop, tile_bytes(q0, L.lq, a.dos.s, D, 2));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i)
+      if (QCH % NT == 0 || tid + NT * i < QCH) {  // rows at or past lq read as zero
+        qreg[i] = buf_load16(qr, qoff[i]);
+        dreg[i] = buf_load16(dr, doff[i]);
+      }
     if (tid < kQTile) {
       const int qi = q0 + tid;
       const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + qi;
@@ -354,10 +293,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   for (int it = 0; it < n_it; ++it) {
     const int q0 = (qt0 + it % nq) * kQTile;
     __syncthreads();  // every wave is done with the previous tile
-    if (stager) {
-      *(u32x4*)(&Qs[sdst]) = qreg;
-      *(u32x4*)(&Ds_[sdst]) = dreg;
-    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i)
+      if (QCH % NT == 0 || tid + NT * i < QCH) {
+        *(u32x4*)(&Qs[sdst[i]]) = qreg[i];
+        *(u32x4*)(&Ds_[sdst[i]]) = dreg[i];
+      }
     if (tid < kQTile) {
       lse2s[tid] = lreg;
       dels[tid] = creg;
@@ -505,18 +446,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split,
 // dQ
 // ---------------------------------------------------------------------------
 // Pipelined like the forward: the K/V tile of step t+2 is loaded into
-// registers while step t is computed and written to the other LDS buffer
-// (K row-major and transposed, V row-major) at step t+1.
+// registers while step t is computed and written to the other LDS buffer at
+// step t+1. K and V tiles are row-major in the bswz layout; the K^T operand of
+// dQ^T += K^T dS^T comes from the same K tile through ds_read_b64_tr_b16.
 template <typename T, int D, bool CAUSAL, bool MOD>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   typedef typename T::vec8 V8;
-  typedef BlockTile<kKTile, D> KTile;
-  typedef ChunkTile<kKTile, D> VTile;
+  typedef BswzTile<kKTile, D, 256> KvTile;
   constexpr int NKS = D / 16, NDB = D / 32, NSB = kKTile / 32;
-  constexpr int RS = KTile::RS, TS = KTile::TS;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -565,20 +504,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
+  // This lane's row-operand offsets in a K / V tile: row j (+ 32 nb), chunk 2 t + h.
+  int rowoff[NKS];
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) rowoff[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
+  TrLaneB<D> trl;
+  trl.init(lane);
+
   const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + kQBlock, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kKTile - 1) / kKTile;
-  KTile kreg;
-  VTile vreg;
+  KvTile kreg, vreg;
   kreg.init(a.ks.s, tid);
   vreg.init(a.vs.s, tid);
   auto load_tile = [&](int k0) {
-    kreg.load(kp, k0, L.lk, tid);  // keys at or past lk read as zero
-    vreg.load(vp, k0, L.lk, tid);
+    kreg.load(kp, k0, L.lk);  // keys at or past lk read as zero
+    vreg.load(vp, k0, L.lk);
   };
   auto store_tile = [&](int buf) {
-    kreg.store_rm(Ks[buf], tid);
-    kreg.store_tr(Kt[buf], tid);
-    vreg.store(Vs[buf], tid);
+    kreg.store(Ks[buf]);
+    vreg.store(Vs[buf]);
   };
   if (n_tiles > 0) {
     load_tile(0);
@@ -602,9 +546,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       dp[nb] = f32x16{};
 #pragma unroll
       for (int t = 0; t < NKS; ++t) {
-        const V8 ka = *(const V8*)(&Ks[buf][(nb * 32 + j) * RS + 16 * t + 8 * h]);
+        const V8 ka = *(const V8*)(&Ks[buf][nb * 32 * D + rowoff[t]]);
         s[nb] = T::mfma(ka, qf[t], s[nb]);
-        const V8 va = *(const V8*)(&Vs[buf][(nb * 32 + j) * RS + 16 * t + 8 * h]);
+        const V8 va = *(const V8*)(&Vs[buf][nb * 32 * D + rowoff[t]]);
         dp[nb] = T::mfma(va, df[t], dp[nb]);
       }
     }
@@ -665,10 +609,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       const V8 sb = __builtin_bit_cast(
           V8, u32x4{dspk[nb][base], dspk[nb][base + 1], dspk[nb][base + 2], dspk[nb][base + 3]});
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const V8 kta = read_tr_operand<V8>(Kt[buf], TS, db * 32 + j, t2, h);
-        dq[db] = T::mfma(kta, sb, dq[db]);
-      }
+      for (int db = 0; db < NDB; ++db) dq[db] = T::mfma(trl.template tr<V8>(Ks[buf], db, t2), sb, dq[db]);
     }
   }
   if (my_q < a.s_q) {

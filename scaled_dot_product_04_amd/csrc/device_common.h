@@ -78,13 +78,6 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// Row-major LDS tiles read both as MFMA row operands (ds_read_b128 of one
-// row by 8 consecutive lanes) and transposed (ds_read_b64_tr_b16 of 4
-// consecutive rows x 32 bytes by a 16-lane group) store 16-byte chunk c of row
-// r at chunk position c ^ swz(r), with no row padding. With rows a multiple of
-// 128 bytes, both access patterns then touch distinct banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
@@ -155,20 +148,6 @@ __device__ __forceinline__ float wave_max_halves(float x) {
   return fmaxf(x, __shfl_xor(x, 32, 64));
 }
 __device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
-
-// 4x4 transpose of 16-bit elements held as 4 rows of (lo, hi) dwords:
-// in: row r = (e[r][0] | e[r][1] << 16, e[r][2] | e[r][3] << 16)
-// out: column c = (e[0][c] | e[1][c] << 16, e[2][c] | e[3][c] << 16)
-__device__ __forceinline__ void transpose4x4_b16(const u32x2 in[4], u32x2 out[4]) {
-  out[0].x = __builtin_amdgcn_perm(in[1].x, in[0].x, 0x05040100u);
-  out[0].y = __builtin_amdgcn_perm(in[3].x, in[2].x, 0x05040100u);
-  out[1].x = __builtin_amdgcn_perm(in[1].x, in[0].x, 0x07060302u);
-  out[1].y = __builtin_amdgcn_perm(in[3].x, in[2].x, 0x07060302u);
-  out[2].x = __builtin_amdgcn_perm(in[1].y, in[0].y, 0x05040100u);
-  out[2].y = __builtin_amdgcn_perm(in[3].y, in[2].y, 0x05040100u);
-  out[3].x = __builtin_amdgcn_perm(in[1].y, in[0].y, 0x07060302u);
-  out[3].y = __builtin_amdgcn_perm(in[3].y, in[2].y, 0x07060302u);
-}
 
 // Chunk swizzle of the row-major V tile: row r keeps its 16-byte chunk c at
 // position c ^ vswz<D>(r). The LDS serves a 64-lane 8-byte read in two passes
