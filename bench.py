@@ -90,7 +90,8 @@ def cpu_baseline(w, ins, n_heads: int) -> dict:
 
 
 TRAFFIC_RECORDS = {"bwd_dkdv": "profiles/hd128_causal_s8192_dkdv_hbm_traffic.json",
-                   "fwd": "profiles/hd128_causal_s8192_fwd_hbm_traffic.json"}
+                   "fwd": "profiles/hd128_causal_s8192_fwd_hbm_traffic.json",
+                   "bwd_dq": "profiles/hd128_causal_s8192_dq_hbm_traffic.json"}
 
 
 def sources_digest(paths) -> str:
@@ -159,6 +160,85 @@ def write_traffic_record(kernel: str, fetch_db: str, write_db: str, copy_fetch_d
         json.dump(rec, f, indent=1)
         f.write("\n")
     return out
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    m = re.search(r"(\w+_kernel)(<[^()]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")).replace("sdpa::", "") if m else name[:60]
+
+
+def summarize_trace(db: str, last: int = 0) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace result database: per kernel,
+    launches, total, mean and median duration (us); with last > 0 also the mean
+    of the last `last` launches of each kernel (the timed steps after warm-up).
+    No GPU use."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    per = {}
+    for name, start, end in c.execute("select name, start, end from kernels"):
+        per.setdefault(_short_kernel(name), []).append((start, (end - start) / 1000.0))
+    total = sum(d for v in per.values() for _, d in v)
+    lines = ["| kernel | launches | total us | mean us | median us | % of GPU time |"
+             + (f" mean of last {last} us |" if last else ""),
+             "|---|---|---|---|---|---|" + ("---|" if last else "")]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = [x for _, x in sorted(v)]
+        row = (f"| `{k}` | {len(d)} | {sum(d):.1f} | {statistics.fmean(d):.1f} | {statistics.median(d):.1f} | "
+               f"{100 * sum(d) / total:.1f} |")
+        if last:
+            row += f" {statistics.fmean(d[-last:]):.1f} |"
+        lines.append(row)
+    return "\n".join(lines)
+
+
+def summarize_counters(dbs: list) -> str:
+    """Markdown table of rocprofv3 --pmc result databases: per kernel, the
+    median per dispatch of every counter collected, and where the counters
+    allow it the derived clock (GRBM_GUI_ACTIVE per XCD over the dispatch
+    duration) and MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+    1024 SIMDs x clock x duration). No GPU use."""
+    import sqlite3
+    per = {}
+    for db in dbs:
+        c = sqlite3.connect(db)
+        for kn, cn, did, v, dur in c.execute(
+                "select kernel_name, counter_name, dispatch_id, value, duration from counters_collection"):
+            k = _short_kernel(kn)
+            ent = per.setdefault(k, {}).setdefault((db, did), {"dur": dur})
+            ent[cn] = ent.get(cn, 0.0) + v
+    out = []
+    for k, disp in sorted(per.items()):
+        vals = {}
+        for ent in disp.values():
+            for cn, v in ent.items():
+                vals.setdefault(cn, []).append(v)
+        med = {cn: statistics.median(v) for cn, v in vals.items()}
+        out.append(f"`{k}` ({len(disp)} dispatch records)")
+        out.append("")
+        out.append("| counter | median per dispatch |")
+        out.append("|---|---|")
+        for cn in sorted(med):
+            if cn != "dur":
+                out.append(f"| {cn} | {med[cn]:.6g} |")
+        # Rates per dispatch record (counter / that record's duration), then medians.
+        def rate(cn, div):
+            r = [e[cn] / div / (e["dur"] / 1e9) for e in disp.values() if cn in e and e["dur"] > 0]
+            return statistics.median(r) if r else None
+        clk = rate("GRBM_GUI_ACTIVE", 8)
+        if clk is not None:
+            out.append(f"| clock: GRBM_GUI_ACTIVE / 8 XCDs / duration | {clk / 1e9:.2f} GHz |")
+        clk2 = rate("SQ_CYCLES", 32)
+        if clk2 is not None:
+            out.append(f"| clock: SQ_CYCLES / 32 SEs / duration | {clk2 / 1e9:.2f} GHz |")
+        busy = rate("SQ_VALU_MFMA_BUSY_CYCLES", 1024)
+        if busy is not None and (clk or clk2):
+            f = clk or clk2
+            out.append(f"| MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x clock x duration) | "
+                       f"{100 * busy / f:.1f} % |")
+            out.append(f"| same, against the 2.4 GHz clock of the published peak | {100 * busy / 2.4e9:.1f} % |")
+        out.append("")
+    return "\n".join(out)
 
 
 def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
@@ -303,11 +383,79 @@ def varlen_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: i
     return res
 
 
+def config_sweep(sdpa, sdpa_inputs, torch, hip, warmup: int, steps: int) -> list:
+    """Full-size timing of every workload the parity tests cover: the hd128
+    causal sweep (s = 512 .. 16384, b = 16384 / s), GQA / MQA (h_q 32,
+    h_kv 32 / 8 / 1), the GPT-2-like fp16 forward and the fp8 hd256 forward.
+    One dict per workload: forward (and forward + backward) ms and TFLOP/s of
+    the counted flops, against the dtype's dense peak, after a warm-up of at
+    least 0.3 s of the same calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ws = [sdpa_inputs.hd128(s) for s in sdpa_inputs.HD128_SEQS]
+    ws += [sdpa_inputs.gqa(h) for h in (32, 8, 1)] + [sdpa_inputs.gpt2(), sdpa_inputs.fp8()]
+    out = []
+    for w in ws:
+        ins = sdpa_inputs.make_inputs(w, with_grad=w.backward)
+        g = {k: sdpa_inputs.to_device_like(v, dev) for k, v in ins.items() if isinstance(v, torch.Tensor)}
+        fp8 = None
+        if w.dtype == "fp8":
+            fp8 = sdpa.Fp8Scales(ins["descale_q"], ins["descale_k"], ins["descale_v"], ins["scale_p"],
+                                 ins["descale_p"])
+        o = sdpa._like_q(g["q"], torch.bfloat16 if w.dtype == "fp8" else g["q"].dtype)
+        lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+        peak = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
+        res = {"workload": w.name, "b": w.b, "h_q": w.h_q, "h_kv": w.h_kv, "s": w.s_q, "d": w.d,
+               "dtype": w.dtype, "causal": w.causal}
+
+        def fwd():
+            sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, out=o, lse=lse, fp8=fp8, stream=stream)
+
+        fns = [("forward", fwd, 1.0)]
+        if w.backward:
+            dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+            wsp = torch.empty(max(16, sdpa.bwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, w.causal,
+                                                              g["q"].dtype)), dtype=torch.uint8, device=dev)
+
+            def step():
+                fwd()
+                sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk,
+                         dv=dv, workspace=wsp, stream=stream)
+            fns.append(("forward_backward", step, 3.5))
+        for name, fn, mult in fns:
+            # The GPU clock ramps up over the first ~20 ms of sustained work:
+            # warm up for at least 0.3 s as well as `warmup` calls.
+            t0, n = time.perf_counter(), 0
+            while n < warmup or time.perf_counter() - t0 < 0.3:
+                fn()
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
+            a, b = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            hip.record(a, sh)
+            for _ in range(steps):
+                fn()
+            hip.record(b, sh)
+            torch.cuda.synchronize()
+            ms = hip.ms(a, b) / steps
+            tf = mult * w.fwd_flops / (ms / 1e3) / 1e12
+            res[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "pct_peak": round(100 * tf / peak, 2)}
+        log(f"[bench] {res}")
+        out.append(res)
+        del g, o, lse, ins
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The GPU clock ramps up over the first ~100 ms of sustained work: the
+    # default warm-up (about 0.14 s of steps) times the kernels at steady clocks.
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
@@ -318,10 +466,23 @@ def main() -> int:
                                                           "COPY_WRITE_DB"),
                     help="write the HBM-traffic record of KERNEL from rocprofv3 --pmc result databases and exit "
                          "(no GPU use)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print a markdown table of a rocprofv3 --kernel-trace result database and exit (no GPU use)")
+    ap.add_argument("--last", type=int, default=0, help="with --summarize-trace: also average the last N launches")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DB",
+                    help="print markdown tables of rocprofv3 --pmc result databases and exit (no GPU use)")
+    ap.add_argument("--config-sweep", action="store_true",
+                    help="time every full-size workload of the parity tests (one JSON object per line) and exit")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.last))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return 0
     if args.traffic_record:
         k, f_db, w_db, cf_db, cw_db = args.traffic_record
         cmds = [f"rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-heads 0 "
@@ -354,6 +515,11 @@ def main() -> int:
 
     import scaled_dot_product_04_amd as sdpa
     import sdpa_inputs
+
+    if args.config_sweep:
+        for res in config_sweep(sdpa, sdpa_inputs, torch, Hip(), args.warmup, args.steps):
+            print(json.dumps(res), flush=True)
+        return 0
 
     w = sdpa_inputs.hd128(args.seq)
     log(f"[bench] workload {w.name}: b={w.b} h={w.h_q} s={w.s_q} d={w.d} bf16 causal BSHD")
