@@ -56,7 +56,13 @@ __device__ __forceinline__ void transpose4x4_b8(const uint32_t in[4], uint32_t o
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(FwdArgs a, int n_qblk) {
+// Occupancy: two workgroups per CU at d = 256 (256 VGPRs, 2 x 74 KB LDS) and
+// three at d = 128 (168 VGPRs): a second (third) wave per SIMD hides the
+// softmax VALU work behind the other waves' MFMAs. The few VGPRs this spills
+// (staging offsets, reloaded from scratch a few times per key tile) cost far
+// less: same-box A/B at d = 256 (b4 h8 s8192), 2.28 ms with one wave per
+// SIMD, 1.86 ms with two.
+__global__ __launch_bounds__(64 * kNW, D == 256 ? 2 : 3) void fwd_fp8_kernel(FwdArgs a, int n_qblk) {
   constexpr int NT = 64 * kNW;
   constexpr int KSTR = D + 16;       // bytes per K row in LDS
   constexpr int VSTR = kBN8 + 16;    // bytes per transposed V row in LDS
