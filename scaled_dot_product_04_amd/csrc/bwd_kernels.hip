@@ -171,7 +171,7 @@ struct BswzTile {
 // registers while the current one is computed. The transposed Q^T / dO^T
 // operands of dK and dV are read from the same row-major tiles with
 // ds_read_b64_tr_b16.
-template <typename T, int D, bool CAUSAL, bool MOD>
+template <typename T, int D, bool CAUSAL, int MOD>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk, int n_split, float* part) {
   typedef typename T::vec8 V8;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     // Score modifiers of this query head (log2 units), applied per row group below.
     const int hq_it = hq_base + it / nq;
     const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq_it] * kLog2e : 0.f;
-    const char* bias_bh = (MOD && a.mod.bias != nullptr)
+    const char* bias_bh = (MOD == kModAll && a.mod.bias != nullptr)
                               ? (const char*)a.mod.bias + (bi * a.mod.bb + hq_it * a.mod.bh) * (a.mod.bias_f32 ? 4 : 2)
                               : nullptr;
     uint32_t ppk[8], dspk[8];
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
       const f32x4 l4 = *(const f32x4*)(&lse2s[row0]);
       const f32x4 d4 = *(const f32x4*)(&dels[row0]);
       // Dropout words of queries q0 + row0 .. +3 (one per query) at this key.
-      const u32x4 dw = (MOD && a.mod.drop_k8 < 256)
+      const u32x4 dw = (MOD == kModAll && a.mod.drop_k8 < 256)
                            ? drop_words((uint32_t)my_key >> 2, (uint32_t)(q0 + row0) >> 2,
                                         (uint32_t)(bi * a.h_q + hq_it), a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
                            : u32x4{0u, 0u, 0u, 0u};
@@ -351,11 +351,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
           const void* brow = (bias_bh != nullptr && qi < a.s_q)
                                  ? (const void*)(bias_bh + (int64_t)qi * a.mod.bs * (a.mod.bias_f32 ? 4 : 2))
                                  : nullptr;
-          madd = fmaf(bias1<T>(brow, a.mod.bias_f32, my_key, a.s_kv), kLog2e,
-                      -slope2 * fabsf((float)(qi + L.off - my_key)));
+          const float bv = MOD == kModAll ? bias1<T>(brow, a.mod.bias_f32, my_key, a.s_kv) : 0.f;
+          madd = fmaf(bv, kLog2e, -slope2 * fabsf((float)(qi + L.off - my_key)));
         }
         const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, madd - l4[e]));
-        if (MOD) {  // dV takes P Z (Z's scale applied at the end); dS = P (Z dP - D)
+        if (MOD == kModAll) {  // dV takes P Z (Z's scale applied at the end); dS = P (Z dP - D)
           const bool keep = drop_keep(dw[e], my_key & 3, a.mod.drop_k8);
           pv[e] = keep ? p : 0.f;
           dsv[e] = p * ((keep ? a.mod.drop_scale * dp[4 * r4 + e] : 0.f) - d4[e]);
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 
   if (my_key >= a.s_kv) return;
-  const float vsc = MOD ? a.dv_scale * a.mod.drop_scale : a.dv_scale;  // dV = (P Z)^T dO, Z = keep * drop_scale
+  const float vsc = MOD == kModAll ? a.dv_scale * a.mod.drop_scale : a.dv_scale;  // dV = (P Z)^T dO, Z = keep * drop_scale
   if (n_split == 1) {
     uint16_t* dkp = (uint16_t*)a.dk + bi * a.dks.b + g * a.dks.h + (int64_t)my_key * a.dks.s;
     uint16_t* dvp = (uint16_t*)a.dv + bi * a.dvs.b + g * a.dvs.h + (int64_t)my_key * a.dvs.s;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split,
 // registers while step t is computed and written to the other LDS buffer at
 // step t+1. K and V tiles are row-major in the bswz layout; the K^T operand of
 // dQ^T += K^T dS^T comes from the same K tile through ds_read_b64_tr_b16.
-template <typename T, int D, bool CAUSAL, bool MOD>
+template <typename T, int D, bool CAUSAL, int MOD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   typedef typename T::vec8 V8;
   typedef BswzTile<kKTile, D, 256> KvTile;
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   const float dl = my_q < L.lq ? a.delta[row_bh + my_q] : 0.f;
   const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
   const void* bias_row =
-      (MOD && a.mod.bias != nullptr && my_q < a.s_q)
+      (MOD == kModAll && a.mod.bias != nullptr && my_q < a.s_q)
           ? (const void*)((const char*)a.mod.bias +
                           (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * (a.mod.bias_f32 ? 4 : 2))
           : nullptr;
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
-          const f32x4 bv = bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv);
+          const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             madd[nb][4 * q4 + e] = fmaf(bv[e], kLog2e, -slope2 * fabsf((float)(my_q + L.off - (key0 + e))));
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
       uint32_t dw[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        dw[q4] = (MOD && a.mod.drop_k8 < 256)
+        dw[q4] = (MOD == kModAll && a.mod.drop_k8 < 256)
                      ? drop_word((uint32_t)(k0 + nb * 32 + 8 * q4 + 4 * h) >> 2, my_q, (uint32_t)(bi * a.h_q + hq),
                                  a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
                      : 0u;
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, madd[nb][r] - lse2));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, madd[nb][r + 1] - lse2));
         float z0 = 1.f, z1 = 1.f;  // dS = P (Z dP - D)
-        if (MOD) {
+        if (MOD == kModAll) {
           z0 = drop_keep(dw[r / 4], r % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
           z1 = drop_keep(dw[r / 4], (r + 1) % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
         }
@@ -639,7 +639,7 @@ int choose_split(int b, int h_q, int h_kv, int s_kv) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <typename T, int D, bool MOD>
+template <typename T, int D, int MOD>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& te) {
   constexpr int RPB = 256 / (D / 8);
   const bool timed = te.n >= 4;
@@ -690,7 +690,7 @@ hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool MOD>
+template <int MOD>
 hipError_t launch_bwd_m(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
   if (io == Io::BF16)
     return a.d == 64 ? launch_all<Bf16T, 64, MOD>(a, stream, te) : launch_all<Bf16T, 128, MOD>(a, stream, te);
@@ -698,8 +698,11 @@ hipError_t launch_bwd_m(const BwdArgs& a, Io io, hipStream_t stream, const Timin
 }
 
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
-  if (has_mod(a.mod)) return launch_bwd_m<true>(a, io, stream, te);
-  return launch_bwd_m<false>(a, io, stream, te);
+  switch (mod_level(a.mod)) {
+    case kModAll: return launch_bwd_m<kModAll>(a, io, stream, te);
+    case kModAlibi: return launch_bwd_m<kModAlibi>(a, io, stream, te);
+    default: return launch_bwd_m<kModNone>(a, io, stream, te);
+  }
 }
 
 }  // namespace sdpa

@@ -47,8 +47,9 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 
 
 // NW waves per workgroup, 32 query rows per wave. MOD: score modifiers
+// (kModAlibi: ALiBi slopes only; kModAll: bias tensor, ALiBi, dropout)
 // (bias tensor and/or ALiBi) are added to the scaled scores.
-template <typename T, int D, bool CAUSAL, int NW, bool MOD>
+template <typename T, int D, bool CAUSAL, int NW, int MOD>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
   typedef typename T::elem E;
   typedef typename T::vec8 V8;
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // reduction and loop overhead; 246 VGPRs, 135 KB LDS at 8 waves), 64 at
   // d = 64 (keeps three waves per SIMD) and with score modifiers (their
   // registers would not fit beside 128-key score tiles).
-  constexpr int kBN = (D == 128 && !MOD) ? 128 : 64;
+  constexpr int kBN = (D == 128 && MOD == kModNone) ? 128 : 64;
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
   const uint32_t drop_slot = (uint32_t)(bi * a.h_q + hq);
   const void* bias_row =
-      (MOD && a.mod.bias != nullptr && my_q < a.s_q)
+      (MOD == kModAll && a.mod.bias != nullptr && my_q < a.s_q)
           ? (const void*)((const char*)a.mod.bias +
                           (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * (a.mod.bias_f32 ? 4 : 2))
           : nullptr;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
-          const f32x4 bv = bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv);
+          const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
         lsum0 += p0;  // the row sum uses the undropped weights
         lsum1 += p1;
-        if (MOD) {
+        if (MOD == kModAll) {
           // Dropout word of this row for the 4-key group of r (0, i.e. every
           // byte kept, without dropout).
           const uint32_t dw = (a.mod.drop_k8 < 256)
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // no key, get O = 0 and LSE = -inf.
   const float l_tot = wave_sum_halves(l_run);
   const bool live = my_q < L.lq && l_tot > 0.f;
-  const float inv = live ? (MOD ? a.mod.drop_scale : 1.f) / l_tot : 0.f;
+  const float inv = live ? (MOD == kModAll ? a.mod.drop_scale : 1.f) / l_tot : 0.f;
   if (my_q < a.s_q) {
     E* op = (E*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   }
 }
 
-template <typename T, int D, int NW, bool MOD>
+template <typename T, int D, int NW, int MOD>
 hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
   const int bm = 32 * NW;
   const int n_qblk = (a.s_q + bm - 1) / bm;
@@ -408,8 +409,11 @@ hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int NW>
 hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
-  if (has_mod(a.mod)) return launch_mfma_dm<T, D, NW, true>(a, stream);
-  return launch_mfma_dm<T, D, NW, false>(a, stream);
+  switch (mod_level(a.mod)) {
+    case kModAll: return launch_mfma_dm<T, D, NW, kModAll>(a, stream);
+    case kModAlibi: return launch_mfma_dm<T, D, NW, kModAlibi>(a, stream);
+    default: return launch_mfma_dm<T, D, NW, kModNone>(a, stream);
+  }
 }
 
 template <int D>

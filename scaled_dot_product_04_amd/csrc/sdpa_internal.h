@@ -32,6 +32,15 @@ struct ScoreMod {
 // Whether any modifier is active (the kernels take their MOD variant).
 inline bool has_mod(const ScoreMod& m) { return m.slopes != nullptr || m.bias != nullptr || m.drop_k8 < 256; }
 
+// Kernel variants by score modifier: none, ALiBi slopes only (no loads beyond
+// one slope per head, no random numbers), or the general path (bias tensor,
+// ALiBi, dropout).
+constexpr int kModNone = 0, kModAlibi = 1, kModAll = 2;
+inline int mod_level(const ScoreMod& m) {
+  if (!has_mod(m)) return kModNone;
+  return (m.bias == nullptr && m.drop_k8 >= 256) ? kModAlibi : kModAll;
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
