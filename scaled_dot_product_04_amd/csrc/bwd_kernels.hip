@@ -331,17 +331,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     const char* bias_bh = (MOD == kModAll && a.mod.bias != nullptr)
                               ? (const char*)a.mod.bias + (bi * a.mod.bb + hq_it * a.mod.bh) * (a.mod.bias_f32 ? 4 : 2)
                               : nullptr;
+    // Dropout keep bytes of this lane's key: byte e of kb[r4] is query q0 + 8 r4 + 4 h + e.
+    // The four lanes of a key quad share the tile's four blocks (one per r4):
+    // lane t draws block r4 = t, regroups its bytes per key and the quad
+    // trades them.
+    u32x4 kb = u32x4{0u, 0u, 0u, 0u};
+    if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
+      const uint32_t t = (uint32_t)(lane & 3);
+      const u32x4 w = drop_words((uint32_t)my_key >> 2, (uint32_t)(q0 + 8 * t + 4 * h) >> 2,
+                                 (uint32_t)(bi * a.h_q + hq_it), a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
+      kb = quad_transpose(bytes_transpose4(w), lane);
+    }
     uint32_t ppk[8], dspk[8];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * h;
       const f32x4 l4 = *(const f32x4*)(&lse2s[row0]);
       const f32x4 d4 = *(const f32x4*)(&dels[row0]);
-      // Dropout words of queries q0 + row0 .. +3 (one per query) at this key.
-      const u32x4 dw = (MOD == kModAll && a.mod.drop_k8 < 256)
-                           ? drop_words((uint32_t)my_key >> 2, (uint32_t)(q0 + row0) >> 2,
-                                        (uint32_t)(bi * a.h_q + hq_it), a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
-                           : u32x4{0u, 0u, 0u, 0u};
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -355,8 +361,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
           madd = fmaf(bv, kLog2e, -slope2 * fabsf((float)(qi + L.off - my_key)));
         }
         const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], sl2, madd - l4[e]));
-        if (MOD == kModAll) {  // dV takes P Z (Z's scale applied at the end); dS = P (Z dP - D)
-          const bool keep = drop_keep(dw[e], my_key & 3, a.mod.drop_k8);
+        if (MOD >= kModDrop) {  // dV takes P Z (Z's scale applied at the end); dS = P (Z dP - D)
+          const bool keep = drop_keep(kb[r4], e, a.mod.drop_k8);
           pv[e] = keep ? p : 0.f;
           dsv[e] = p * ((keep ? a.mod.drop_scale * dp[4 * r4 + e] : 0.f) - d4[e]);
         } else {
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 
   if (my_key >= a.s_kv) return;
-  const float vsc = MOD == kModAll ? a.dv_scale * a.mod.drop_scale : a.dv_scale;  // dV = (P Z)^T dO, Z = keep * drop_scale
+  const float vsc = MOD >= kModDrop ? a.dv_scale * a.mod.drop_scale : a.dv_scale;  // dV = (P Z)^T dO, Z = keep * drop_scale
   if (n_split == 1) {
     uint16_t* dkp = (uint16_t*)a.dk + bi * a.dks.b + g * a.dks.h + (int64_t)my_key * a.dks.s;
     uint16_t* dvp = (uint16_t*)a.dv + bi * a.dvs.b + g * a.dvs.h + (int64_t)my_key * a.dvs.s;
@@ -583,19 +589,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
     uint32_t dspk[NSB][8];
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb) {
-      uint32_t dw[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        dw[q4] = (MOD == kModAll && a.mod.drop_k8 < 256)
-                     ? drop_word((uint32_t)(k0 + nb * 32 + 8 * q4 + 4 * h) >> 2, my_q, (uint32_t)(bi * a.h_q + hq),
-                                 a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
-                     : 0u;
+      // Dropout words of this row for the key groups q4 = 0..3: the four lanes
+      // of a query quad draw one block each (q4 = lane & 3) and trade words.
+      u32x4 dw = u32x4{0u, 0u, 0u, 0u};
+      if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
+        const u32x4 w = drop_words((uint32_t)(k0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
+                                   (uint32_t)(bi * a.h_q + hq), a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
+        dw = quad_transpose(w, lane);
+      }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, madd[nb][r] - lse2));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, madd[nb][r + 1] - lse2));
         float z0 = 1.f, z1 = 1.f;  // dS = P (Z dP - D)
-        if (MOD == kModAll) {
+        if (MOD >= kModDrop) {
           z0 = drop_keep(dw[r / 4], r % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
           z1 = drop_keep(dw[r / 4], (r + 1) % 4, a.mod.drop_k8) ? a.mod.drop_scale : 0.f;
         }
@@ -700,6 +707,7 @@ hipError_t launch_bwd_m(const BwdArgs& a, Io io, hipStream_t stream, const Timin
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te) {
   switch (mod_level(a.mod)) {
     case kModAll: return launch_bwd_m<kModAll>(a, io, stream, te);
+    case kModDrop: return launch_bwd_m<kModDrop>(a, io, stream, te);
     case kModAlibi: return launch_bwd_m<kModAlibi>(a, io, stream, te);
     default: return launch_bwd_m<kModNone>(a, io, stream, te);
   }

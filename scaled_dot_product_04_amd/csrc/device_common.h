@@ -255,4 +255,44 @@ __device__ __forceinline__ bool drop_keep(uint32_t word, int byte, int k8) {
   return (int)((word >> (8 * byte)) & 0xFFu) < k8;
 }
 
+// Four lanes that need the same four dropout blocks (a quad of consecutive
+// query rows, or of consecutive keys) each draw one block and trade the
+// parts the others need, instead of all four drawing all four.
+
+// 4x4 transpose of dwords across the lanes of a quad (lanes 4m .. 4m+3): lane
+// L holds a[0..3]; afterwards lane L holds out[k] = a[L] of lane k. Two
+// rounds of DPP exchanges (lane ^ 1, then lane ^ 2) and selects.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 a, int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2;
+  const uint32_t x0 = dpp_xor1(a[1]), x1 = dpp_xor1(a[0]), x2 = dpp_xor1(a[3]), x3 = dpp_xor1(a[2]);
+  u32x4 s;
+  s[0] = b0 ? x0 : a[0];
+  s[1] = b0 ? a[1] : x1;
+  s[2] = b0 ? x2 : a[2];
+  s[3] = b0 ? a[3] : x3;
+  const uint32_t y0 = dpp_xor2(s[2]), y1 = dpp_xor2(s[3]), y2 = dpp_xor2(s[0]), y3 = dpp_xor2(s[1]);
+  u32x4 r;
+  r[0] = b1 ? y0 : s[0];
+  r[1] = b1 ? y1 : s[1];
+  r[2] = b1 ? s[2] : y2;
+  r[3] = b1 ? s[3] : y3;
+  return r;
+}
+
+// 4x4 transpose of the bytes of four dwords: out[t] byte w = in[w] byte t.
+__device__ __forceinline__ u32x4 bytes_transpose4(u32x4 w) {
+  const uint32_t p01l = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+  const uint32_t p01h = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+  const uint32_t p23l = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const uint32_t p23h = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  return u32x4{__builtin_amdgcn_perm(p23l, p01l, 0x05040100u), __builtin_amdgcn_perm(p23l, p01l, 0x07060302u),
+               __builtin_amdgcn_perm(p23h, p01h, 0x05040100u), __builtin_amdgcn_perm(p23h, p01h, 0x07060302u)};
+}
+
 }  // namespace sdpa

@@ -47,7 +47,8 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 
 
 // NW waves per workgroup, 32 query rows per wave. MOD: score modifiers
-// (kModAlibi: ALiBi slopes only; kModAll: bias tensor, ALiBi, dropout)
+// (kModAlibi: ALiBi slopes only; kModDrop: dropout and ALiBi; kModAll: also
+// a bias tensor)
 // (bias tensor and/or ALiBi) are added to the scaled scores.
 template <typename T, int D, bool CAUSAL, int NW, int MOD>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
@@ -238,6 +239,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand
     // (m = -inf only while every score of the row is -inf: P = 0).
     const float msub = m_run == -INFINITY ? 0.f : m_run;
+    // Dropout words of this row for the tile's key groups (nb, q4): the four
+    // lanes of a query quad draw one block each (q4 = lane & 3) and trade words.
+    u32x4 dwq[NSB];
+#pragma unroll
+    for (int nb = 0; nb < NSB; ++nb) {
+      dwq[nb] = u32x4{0u, 0u, 0u, 0u};
+      if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
+        const u32x4 w = drop_words((uint32_t)(k0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
+                                   drop_slot, a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
+        dwq[nb] = quad_transpose(w, lane);
+      }
+    }
     uint32_t pk[NSB][8];
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
@@ -248,13 +261,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
         lsum0 += p0;  // the row sum uses the undropped weights
         lsum1 += p1;
-        if (MOD == kModAll) {
+        if (MOD >= kModDrop) {
           // Dropout word of this row for the 4-key group of r (0, i.e. every
-          // byte kept, without dropout).
-          const uint32_t dw = (a.mod.drop_k8 < 256)
-                                  ? drop_word((uint32_t)(k0 + nb * 32 + 8 * (r / 4) + 4 * h) >> 2, my_q, drop_slot,
-                                              a.mod.offset, a.mod.seed_lo, a.mod.seed_hi)
-                                  : 0u;
+          // byte kept, without dropout); byte r % 4 decides key r.
+          const uint32_t dw = dwq[nb][r / 4];
           const bool k_0 = drop_keep(dw, r % 4, a.mod.drop_k8);
           const bool k_1 = drop_keep(dw, (r + 1) % 4, a.mod.drop_k8);
           pk[nb][r / 2] = pack2<T>(k_0 ? p0 : 0.f, k_1 ? p1 : 0.f);
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // no key, get O = 0 and LSE = -inf.
   const float l_tot = wave_sum_halves(l_run);
   const bool live = my_q < L.lq && l_tot > 0.f;
-  const float inv = live ? (MOD == kModAll ? a.mod.drop_scale : 1.f) / l_tot : 0.f;
+  const float inv = live ? (MOD >= kModDrop ? a.mod.drop_scale : 1.f) / l_tot : 0.f;
   if (my_q < a.s_q) {
     E* op = (E*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
 #pragma unroll
@@ -411,6 +421,7 @@ template <typename T, int D, int NW>
 hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
   switch (mod_level(a.mod)) {
     case kModAll: return launch_mfma_dm<T, D, NW, kModAll>(a, stream);
+    case kModDrop: return launch_mfma_dm<T, D, NW, kModDrop>(a, stream);
     case kModAlibi: return launch_mfma_dm<T, D, NW, kModAlibi>(a, stream);
     default: return launch_mfma_dm<T, D, NW, kModNone>(a, stream);
   }

@@ -32,13 +32,14 @@ struct ScoreMod {
 // Whether any modifier is active (the kernels take their MOD variant).
 inline bool has_mod(const ScoreMod& m) { return m.slopes != nullptr || m.bias != nullptr || m.drop_k8 < 256; }
 
-// Kernel variants by score modifier: none, ALiBi slopes only (no loads beyond
-// one slope per head, no random numbers), or the general path (bias tensor,
-// ALiBi, dropout).
-constexpr int kModNone = 0, kModAlibi = 1, kModAll = 2;
+// Kernel variants by score modifier: none; ALiBi slopes only (no loads beyond
+// one slope per head, no random numbers); dropout, with or without ALiBi (no
+// bias loads); the general path (a bias tensor, with ALiBi and dropout).
+constexpr int kModNone = 0, kModAlibi = 1, kModDrop = 2, kModAll = 3;
 inline int mod_level(const ScoreMod& m) {
   if (!has_mod(m)) return kModNone;
-  return (m.bias == nullptr && m.drop_k8 >= 256) ? kModAlibi : kModAll;
+  if (m.bias != nullptr) return kModAll;
+  return m.drop_k8 < 256 ? kModDrop : kModAlibi;
 }
 
 struct FwdArgs {
