@@ -542,7 +542,7 @@ def main() -> int:
             lib.sdpa_set_timing_events((ctypes.c_void_p * 2)(*ev[0:2]), 2)
         sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, stream=stream)
         if ev is not None:
-            lib.sdpa_set_timing_events((ctypes.c_void_p * 4)(*ev[2:6]), 4)
+            lib.sdpa_set_timing_events((ctypes.c_void_p * 3)(*ev[2:5]), 3)
         sdpa.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv,
                  workspace=ws, stream=stream)
         if ev is not None:
@@ -550,7 +550,7 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    events = [[hip.event().value for _ in range(6)] for _ in range(args.steps)]
+    events = [[hip.event().value for _ in range(5)] for _ in range(args.steps)]
     start, stop = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -563,12 +563,11 @@ def main() -> int:
     total_ms = hip.ms(start, stop)
     ms_step = total_ms / args.steps
 
-    per = {"fwd": [], "bwd_delta": [], "bwd_dkdv": [], "bwd_dq": []}
+    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
     for ev in events:
         per["fwd"].append(hip.ms(ev[0], ev[1]))
-        per["bwd_delta"].append(hip.ms(ev[2], ev[3]))
+        per["bwd_dq"].append(hip.ms(ev[2], ev[3]))     # dQ, with D = rowsum(dO * O)
         per["bwd_dkdv"].append(hip.ms(ev[3], ev[4]))
-        per["bwd_dq"].append(hip.ms(ev[4], ev[5]))
     mean = {k: statistics.fmean(v) for k, v in per.items()}
     med = {k: statistics.median(v) for k, v in per.items()}
 
@@ -576,7 +575,7 @@ def main() -> int:
     step_flops = 3.5 * F                 # forward + backward (2.5x)
     value = step_flops / (ms_step / 1e3) / 1e12
     fwd_tflops = F / (med["fwd"] / 1e3) / 1e12
-    bwd_ms = med["bwd_delta"] + med["bwd_dkdv"] + med["bwd_dq"]
+    bwd_ms = med["bwd_dkdv"] + med["bwd_dq"]
     bwd_tflops = 2.5 * F / (bwd_ms / 1e3) / 1e12
     # matmul flops each kernel performs per launch (per (b, h) head: s_q*s_kv*d*2 per matmul, halved causal)
     mm = F / 2.0

@@ -326,10 +326,10 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
  * (n = 0 or events = NULL disables) that this thread's following sdpa_fwd /
  * sdpa_bwd calls record on their stream at kernel boundaries:
  *   sdpa_fwd: events[0] before its kernel, events[1] after it (n >= 2);
- *   sdpa_bwd: events[0] before the D = rowsum(dO * O) kernel, events[1] after
- *             it, events[2] after the dK/dV kernel (and its split reduction),
- *             events[3] after the dQ kernel (n >= 4); sdpa_bwd_fp8 records
- *             the same four after its widening kernels.
+ *   sdpa_bwd: events[0] before the dQ kernel (which also forms
+ *             D = rowsum(dO * O)), events[1] after it, events[2] after the
+ *             dK/dV kernel and its split reduction (n >= 3); sdpa_bwd_fp8
+ *             records the same three after its widening kernels.
  * The library does not own the events. Returns SDPA_ERR_INVALID_ARGUMENT for
  * n < 0, n > 8, or events == NULL with n > 0.
  */

@@ -12,8 +12,11 @@
 // with dK/dV summed over the query heads that share a KV head (JAX attention
 // codelab, step 9: KV heads shared by a group of query heads).
 //
-// Kernels (all atomic-free and deterministic):
-//  1. delta:  D = rowsum(dO * O) in fp32 (memory-bound).
+// Kernels (all atomic-free and deterministic), in launch order:
+//  1. dQ:     Q-stationary, laid out like the forward: each lane owns one
+//     query column of S^T = K Q^T; dQ^T += K^T dS^T with K^T read from the
+//     row-major K tile through ds_read_b64_tr_b16. It also forms
+//     D = rowsum(dO * O) of its rows (fp32) and leaves it in the workspace.
 //  2. dK/dV:  KV-stationary. A workgroup owns 256 keys (32 per wave) whose K
 //     and V rows stay in LDS; it loops over the query heads of its group and
 //     over 32-row query tiles staged row-major in LDS, read both as row
@@ -23,9 +26,6 @@
 //     When a GQA/MQA group would leave the GPU underfilled, the group's query
 //     heads are split over several workgroups that write fp32 partials.
 //  3. reduce: sums the partials of the splits in a fixed order.
-//  4. dQ:     Q-stationary, laid out like the forward: each lane owns one
-//     query column of S^T = K Q^T; dQ^T += K^T dS^T with K^T read from the
-//     row-major K tile through ds_read_b64_tr_b16.
 #include "device_common.h"
 #include "sdpa_internal.h"
 
@@ -37,37 +37,6 @@ constexpr int kKvBlock = 256;  // keys per dK/dV workgroup (8 waves x 32)
 constexpr int kQTile = 32;     // query rows per dK/dV inner step
 constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
 constexpr int kKTile = 32;     // keys per dQ inner step
-
-// D_i = sum_d dO_id * O_id (fp32); a group of d/8 lanes per row, 16-byte loads.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;      // lanes per row
-  constexpr int RPB = 256 / LPR;  // rows per block
-  const int tid = threadIdx.x;
-  const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;
-  const int part = tid % LPR;
-  const int64_t total = (int64_t)a.b * a.h_q * a.s_q;
-  float acc = 0.f;
-  if (r < total) {
-    const int i = (int)(r % a.s_q);
-    const int64_t bh = r / a.s_q;
-    const int hq = (int)(bh % a.h_q), bi = (int)(bh / a.h_q);
-    const int lq = a.seq_q ? min(max(a.seq_q[bi], 0), a.s_q) : a.s_q;
-    if (i < lq) {  // padded rows keep D = 0; their O and dO are never read
-      const uint16_t* op = (const uint16_t*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)i * a.os.s + part * 8;
-      const uint16_t* dp = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)i * a.dos.s + part * 8;
-      const u32x4 ov = *(const u32x4*)op, dv = *(const u32x4*)dp;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = fmaf(to_f32<T>((uint16_t)(ov[w] & 0xffff)), to_f32<T>((uint16_t)(dv[w] & 0xffff)), acc);
-        acc = fmaf(to_f32<T>((uint16_t)(ov[w] >> 16)), to_f32<T>((uint16_t)(dv[w] >> 16)), acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (r < total && part == 0) a.delta[r] = acc * a.delta_scale;
-}
 
 // Writes zeros to dK and dV (problems with no query rows).
 __global__ __launch_bounds__(256) void zero_dkdv_kernel(BwdArgs a) {
@@ -497,7 +466,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   // no key has LSE = -inf and every score masked: 0 keeps its P at 0.
   const float lse = my_q < L.lq ? a.lse[row_bh + my_q] : 0.f;
   const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
-  const float dl = my_q < L.lq ? a.delta[row_bh + my_q] : 0.f;
+  // D = rowsum(dO * O) of this row: this lane holds half of the row's dO
+  // (elements 16 t + 8 h .. +7) and reads the same half of O; the halves are
+  // summed across the wave. The dK/dV kernel, launched next, reads D from the
+  // workspace (rows past lq hold 0 and are never used).
+  float dpart = 0.f;
+  if (my_q < L.lq) {
+    const uint16_t* op = (const uint16_t*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
+#pragma unroll
+    for (int t = 0; t < NKS; ++t) {
+      const u32x4 ov = *(const u32x4*)(op + 16 * t + 8 * h);
+      const u32x4 dv = __builtin_bit_cast(u32x4, df[t]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dpart = fmaf(to_f32<T>((uint16_t)(ov[w] & 0xffff)), to_f32<T>((uint16_t)(dv[w] & 0xffff)), dpart);
+        dpart = fmaf(to_f32<T>((uint16_t)(ov[w] >> 16)), to_f32<T>((uint16_t)(dv[w] >> 16)), dpart);
+      }
+    }
+  }
+  const float dl = wave_sum_halves(dpart) * a.delta_scale;
+  if (h == 0 && my_q < a.s_q) a.delta[row_bh + my_q] = dl;
   const float slope2 = (MOD && a.mod.slopes != nullptr) ? a.mod.slopes[hq] * kLog2e : 0.f;
   const void* bias_row =
       (MOD == kModAll && a.mod.bias != nullptr && my_q < a.s_q)
@@ -648,11 +636,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T, int D, int MOD>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& te) {
-  constexpr int RPB = 256 / (D / 8);
-  const bool timed = te.n >= 4;
+  const bool timed = te.n >= 3;
   const int64_t rows = (int64_t)a.b * a.h_q * a.s_q;
+  // dQ first: it also writes D = rowsum(dO * O), which dK/dV reads.
   if (timed) (void)hipEventRecord(te.ev[0], stream);
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  const int n_qblk = (a.s_q + kQBlock - 1) / kQBlock;
+  const dim3 g2(n_qblk * a.b * a.h_q);
+  if (a.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
   if (timed) (void)hipEventRecord(te.ev[1], stream);
 
   const int n_split = choose_split(a.b, a.h_q, a.h_kv, a.s_kv);
@@ -670,13 +663,6 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
                        stream, a, n_split, (const float*)part);
   }
   if (timed) (void)hipEventRecord(te.ev[2], stream);
-  const int n_qblk = (a.s_q + kQBlock - 1) / kQBlock;
-  const dim3 g2(n_qblk * a.b * a.h_q);
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
-  if (timed) (void)hipEventRecord(te.ev[3], stream);
   return hipGetLastError();
 }
 
