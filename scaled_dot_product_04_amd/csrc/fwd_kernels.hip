@@ -46,10 +46,9 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 }
 
 
-// NW waves per workgroup, 32 query rows per wave. MOD: score modifiers
-// (kModAlibi: ALiBi slopes only; kModDrop: dropout and ALiBi; kModAll: also
-// a bias tensor)
-// (bias tensor and/or ALiBi) are added to the scaled scores.
+// NW waves per workgroup, 32 query rows per wave. MOD: score modifiers added
+// to the scaled scores (kModAlibi: ALiBi slopes only; kModDrop: dropout and
+// ALiBi; kModAll: also a bias tensor).
 template <typename T, int D, bool CAUSAL, int NW, int MOD>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
   typedef typename T::elem E;
@@ -60,7 +59,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // reduction and loop overhead; 246 VGPRs, 135 KB LDS at 8 waves), 64 at
   // d = 64 (keeps three waves per SIMD) and with score modifiers (their
   // registers would not fit beside 128-key score tiles).
-  constexpr int kBN = (D == 128 && MOD == kModNone) ? 128 : 64;
+  constexpr int kBN = (D == 128 && MOD == kModNone && NW == 8) ? 128 : 64;
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
@@ -448,15 +447,20 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-#ifndef SDPA_FWD_WAVES
-#define SDPA_FWD_WAVES 8
-#endif
+// Up to 1024 keys the d = 128 forward runs 4-wave workgroups with 64-key tiles
+// (two workgroups per CU, 67 KB LDS each): more of them in flight hides the
+// prologue of these short blocks. Same-box sweep: s = 1024 0.130 -> 0.116 ms,
+// s = 512 0.084 -> 0.080 ms; from s = 2048 on the 8-wave, 128-key kernel wins.
+constexpr int kFwdSmallKeys = 1024;
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream) {
-  constexpr int NW = SDPA_FWD_WAVES;
-  if (io == Io::BF16)
-    return a.d == 64 ? launch_mfma_d<Bf16T, 64, 4>(a, stream) : launch_mfma_d<Bf16T, 128, NW>(a, stream);
-  return a.d == 64 ? launch_mfma_d<F16T, 64, 4>(a, stream) : launch_mfma_d<F16T, 128, NW>(a, stream);
+  const bool small = a.s_kv <= kFwdSmallKeys;
+  if (io == Io::BF16) {
+    if (a.d == 64) return launch_mfma_d<Bf16T, 64, 4>(a, stream);
+    return small ? launch_mfma_d<Bf16T, 128, 4>(a, stream) : launch_mfma_d<Bf16T, 128, 8>(a, stream);
+  }
+  if (a.d == 64) return launch_mfma_d<F16T, 64, 4>(a, stream);
+  return small ? launch_mfma_d<F16T, 128, 4>(a, stream) : launch_mfma_d<F16T, 128, 8>(a, stream);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
