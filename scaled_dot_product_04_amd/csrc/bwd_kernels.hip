@@ -233,7 +233,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   u32x4 qreg[QPT], dreg[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) qreg[i] = dreg[i] = u32x4{0, 0, 0, 0};
+  // LSE and D of the next tile's rows, raw as loaded: nothing uses them before
+  // they are staged at the next iteration, so the loads stay in flight through
+  // this tile's compute (a use here would make the wave wait for every load
+  // of the prefetch, and the whole workgroup for that wave at the barrier).
   float lreg = 0.f, creg = 0.f;
+  bool lvalid = false;
   auto load_tile = [&](int it) {
     const int hq = hq_base + it / nq;
     const int q0 = (qt0 + it % nq) * kQTile;
@@ -247,14 +252,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         qreg[i] = buf_load16(qr, qoff[i]);
         dreg[i] = buf_load16(dr, doff[i]);
       }
-    if (tid < kQTile) {
+    if (tid < kQTile) {  // rows past lq read row lq - 1 (any valid row) and are zeroed when staged
       const int qi = q0 + tid;
-      const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + qi;
-      // A row that sees no key has LSE = -inf; all its scores are masked, and
-      // 0 here keeps exp2(-inf - lse) at 0 instead of NaN.
-      const float lse = qi < L.lq ? a.lse[row] : 0.f;
-      lreg = lse == -INFINITY ? 0.f : lse * kLog2e;
-      creg = qi < L.lq ? a.delta[row] : 0.f;
+      lvalid = qi < L.lq;
+      const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + min(qi, L.lq - 1);
+      lreg = a.lse[row];
+      creg = a.delta[row];
     }
   };
 
@@ -269,8 +272,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
         *(u32x4*)(&Ds_[sdst[i]]) = dreg[i];
       }
     if (tid < kQTile) {
-      lse2s[tid] = lreg;
-      dels[tid] = creg;
+      // A row that sees no key has LSE = -inf; all its scores are masked, and
+      // 0 here keeps exp2(-inf - lse) at 0 instead of NaN.
+      lse2s[tid] = (lvalid && lreg != -INFINITY) ? lreg * kLog2e : 0.f;
+      dels[tid] = lvalid ? creg : 0.f;
     }
     if (it + 1 < n_it) load_tile(it + 1);
     __syncthreads();  // this tile is in LDS
