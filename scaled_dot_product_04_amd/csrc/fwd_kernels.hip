@@ -11,17 +11,19 @@
 // tiles through LDS and keeps a running row max m and row sum l (the flash
 // attention recurrence the cuDNN blog's "SDPA performance" section cites).
 //
-// gfx950 design (one workgroup = 4 waves = 128 query rows of one (b, head)):
+// gfx950 design (d = 128: one workgroup = 8 waves = 256 query rows of one
+// (b, head), or 4 waves = 128 rows for up to 1024 keys; d = 64: 4 waves):
 //  * each wave owns 32 query rows; it holds its Q rows in registers as the
 //    B operand of S^T = K Q^T (v_mfma_f32_32x32x16), so every lane owns one
 //    query column of S^T: the row max / row sum of the softmax are in-lane
 //    reductions plus one exchange between the two wave halves;
 //  * the exponentiated scores, packed to 16 bits, are directly the B operand
-//    of O^T += V^T P^T; V^T is read from an LDS copy of the V tile that is
-//    stored transposed (4x4 register transposes during staging);
-//  * K/V tiles of 64 keys are staged in LDS once per workgroup and shared by
-//    the 4 waves; under the causal mask, tiles entirely above the diagonal
-//    are never loaded, and diagonal tiles are masked element-wise;
+//    of O^T += V^T P^T; the V^T operand is read from the row-major V tile
+//    (16-byte chunks swizzled per row) with ds_read_b64_tr_b16;
+//  * K/V tiles (128 keys for the 8-wave d = 128 kernel, else 64) are staged in
+//    LDS once per workgroup through registers, double-buffered, and shared by
+//    the waves; under the causal mask, tiles entirely above the diagonal are
+//    never loaded, and diagonal tiles are masked element-wise;
 //  * workgroups are issued longest-first for the causal mask, and heads are
 //    remapped so that all query blocks of a head (and the query heads of a
 //    GQA group) run on the same XCD and share its L2.
