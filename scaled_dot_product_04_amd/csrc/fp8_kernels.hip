@@ -128,11 +128,18 @@ __global__ __launch_bounds__(64 * kNW, D == 256 ? 2 : 3) void fwd_fp8_kernel(Fwd
     koff[i] = (uint32_t)(r * a.ks.s + cc * 16);
     kdst[i] = r * KSTR + cc * 16;
   }
+  // At d = 256, block c is key group c % 16 of column group c / 16: the 64
+  // lanes of one transposed store then write 16 different 4-byte positions
+  // of only 4 rows (4 lanes per bank; with the column group fastest, the 16
+  // lanes of a key group share a bank). Same-box A/B, b4 h8 s8192: 1.85 ->
+  // 1.27 ms. At d = 128 the column group stays fastest: there the wider
+  // row-contiguous global loads of that order matter more (0.41 vs 0.42 ms).
   uint32_t voff[VBL], vdst[VBL];
 #pragma unroll
   for (int i = 0; i < VBL; ++i) {
     const int c = tid + NT * i;
-    const int cg = c % VCG, kg = c / VCG;   // kg: 4-key group 0..15
+    const int kg = D == 256 ? c % 16 : c / VCG;  // 4-key group 0..15
+    const int cg = D == 256 ? c / 16 : c % VCG;
     voff[i] = (uint32_t)((4 * kg) * a.vs.s + 16 * cg);
     // key 4 kg = 32 blk + 8 gq + 4 hh  ->  position 32 hh + 16 blk + 4 gq
     const int blk = kg >> 3, gq = (kg & 7) >> 1, hh = kg & 1;
