@@ -63,6 +63,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   // registers would not fit beside 128-key score tiles).
   constexpr int kBN = (D == 128 && MOD == kModNone && NW == 8) ? 128 : 64;
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
+  constexpr int kLook = 4;       // MFMAs by which operand reads run ahead
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
   constexpr int NSB = kBN / 32;  // 32-key score blocks per tile
@@ -191,6 +192,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
       }
     }
+    if constexpr (MOD == kModNone) {
+      // Schedule: the K operand reads run kLook MFMAs ahead (the default
+      // schedule read each operand just before its MFMA). 1.5 % on the hd128
+      // forward, no extra spills.
+      __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < NSB * NKS - kLook; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
+    }
     if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
 #pragma unroll
       for (int nb = 0; nb < NSB; ++nb)
@@ -286,6 +299,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         const V8 va = sl.template tr<V8>(Vs[buf], db, t2);
         oacc[db] = T::mfma(va, pb, oacc[db]);
       }
+    }
+    if constexpr (MOD == kModNone) {  // the same for the V^T reads, two per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 1);
+#pragma unroll
+      for (int i = 0; i < (kBN / 16) * NDB - kLook; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLook, 1);
     }
   }
 
