@@ -74,9 +74,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -234,15 +231,6 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     c3 = lo0;
   }
   return u32x4{c0, c1, c2, c3};
-}
-
-// Word (row % 4) of the dropout stream block (row / 4, key / 4): its byte
-// (key % 4) decides element (row, key) (see ScoreMod).
-__device__ __forceinline__ uint32_t drop_word(uint32_t key4, int row, uint32_t slot, uint32_t offset,
-                                              uint32_t seed_lo, uint32_t seed_hi) {
-  const u32x4 w = philox4x32_10(key4, (uint32_t)row >> 2, slot, offset, seed_lo, seed_hi);
-  const int m = row & 3;
-  return m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w;
 }
 
 // The four words of the block (rows row4*4 .. +3, keys key4*4 .. +3).
