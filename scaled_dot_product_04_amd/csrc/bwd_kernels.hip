@@ -56,8 +56,9 @@ __global__ __launch_bounds__(256) void zero_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-// Chunk swizzle of the row-major LDS tiles of the dK/dV kernel (K and V
-// blocks, Q and dO tiles; no row padding): 16-byte chunk c of row r sits at
+// Chunk swizzle of the row-major LDS tiles read both as rows and through
+// transposed reads (the Q and dO tiles of the dK/dV kernel, the K and V tiles
+// of the dQ kernel; no row padding): 16-byte chunk c of row r sits at
 // position c ^ bswz<D>(r). Two access patterns meet it. A 16-byte row read
 // (MFMA row operand) by 16 consecutive lanes touches chunk c of 16
 // consecutive rows; a transposed read (ds_read_b64_tr_b16) by 32 lanes
@@ -134,7 +135,7 @@ struct BswzTile {
 // KV-stationary dK/dV. A workgroup has 8 waves (two per SIMD) and 256 keys;
 // wave w owns keys 32 w .. 32 w + 31 of the block and accumulates their dK^T,
 // dV^T in VGPRs. The block's K and V rows sit in LDS for the whole kernel
-// (128 KB at d = 128); the workgroup walks (query head of its group slice,
+// (132 KB at d = 128); the workgroup walks (query head of its group slice,
 // 32-row query tile) pairs in order, staging each Q / dO tile (and its LSE
 // and D values) in one LDS buffer; the next pair's tile is loaded into
 // registers while the current one is computed. The transposed Q^T / dO^T
@@ -150,10 +151,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   constexpr int QCH = kQTile * CH;            // chunks of one Q (or dO) tile
   constexpr int QPT = (QCH + NT - 1) / NT;    // of which each thread stages up to QPT
   static_assert(KVC * NT == kKvBlock * CH, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint16_t Kb[kKvBlock * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb[kKvBlock * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kQTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds_[kQTile * D];
+  // K/V block: row r holds K row r, then V row r, then 16 bytes of padding.
+  // The pitch is 16 bytes past a multiple of 256, so 16 lanes reading one
+  // 16-byte column chunk of 16 consecutive rows hit 16 distinct bank groups,
+  // and every K and V operand read of a lane is one base plus an immediate.
+  constexpr int KVP = 2 * D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t KV[kKvBlock * KVP];
+  // Q tile, then the dO tile, both in the bswz layout: the dO operands sit at
+  // an immediate offset from the Q operands.
+  __shared__ __attribute__((aligned(16))) uint16_t QD[2 * kQTile * D];
+  uint16_t* const Qs = QD;
+  uint16_t* const Ds_ = QD + kQTile * D;
   __shared__ __attribute__((aligned(16))) float lse2s[kQTile];
   __shared__ __attribute__((aligned(16))) float dels[kQTile];
 
@@ -185,9 +193,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     for (int i = 0; i < KVC; ++i) {
       const int c = tid + NT * i;
       const int r = c / CH, cc = c % CH;
-      const int dst = r * D + ((cc ^ bswz<D>(r)) * 8);
-      *(u32x4*)(&Kb[dst]) = buf_load16(kr, (uint32_t)(r * a.ks.s * 2 + cc * 16));
-      *(u32x4*)(&Vb[dst]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
+      const int dst = r * KVP + cc * 8;
+      *(u32x4*)(&KV[dst]) = buf_load16(kr, (uint32_t)(r * a.ks.s * 2 + cc * 16));
+      *(u32x4*)(&KV[dst + D]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
     }
   }
   f32x16 dk[NDB], dv[NDB];
@@ -207,14 +215,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   const int hq_base = g * G + sp * Gs;
 
   // Per-lane LDS offsets, loop-invariant: this lane's row of the Q / dO tile
-  // (row j) and of the K / V block (row 32 wave + j, the same swizzle since
-  // bswz depends on the row mod 16), chunk 2 t + h.
-  int rowoff_q[NKS], rowoff_k[NKS];
+  // (row j), chunk 2 t + h, and of the K / V block (row 32 wave + j).
+  int rowoff_q[NKS];
 #pragma unroll
-  for (int t = 0; t < NKS; ++t) {
-    rowoff_q[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
-    rowoff_k[t] = (wave * 32 + j) * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
-  }
+  for (int t = 0; t < NKS; ++t) rowoff_q[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
+  const int kvoff = (wave * 32 + j) * KVP + 8 * h;
   TrLaneB<D> trl;
   trl.init(lane);
 
@@ -287,8 +292,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < NKS; ++t) {
-      s = T::mfma(*(const V8*)(&Qs[rowoff_q[t]]), *(const V8*)(&Kb[rowoff_k[t]]), s);
-      dp = T::mfma(*(const V8*)(&Ds_[rowoff_q[t]]), *(const V8*)(&Vb[rowoff_k[t]]), dp);
+      s = T::mfma(*(const V8*)(&Qs[rowoff_q[t]]), *(const V8*)(&KV[kvoff + 16 * t]), s);
+      dp = T::mfma(*(const V8*)(&Ds_[rowoff_q[t]]), *(const V8*)(&KV[kvoff + D + 16 * t]), dp);
     }
     // P and dS; lane owns key my_key, register r owns query q0 + acc_row(r, h).
     const bool need_mask = (q0 + kQTile > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
