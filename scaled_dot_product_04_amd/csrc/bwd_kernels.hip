@@ -533,9 +533,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
     store_tile(0);
     if (n_tiles > 1) load_tile(kKTile);
   }
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // One K/V tile. Unrolled by two, `buf` is a constant at each call, so every
+  // LDS operand address is a per-lane offset plus an immediate instead of an
+  // offset combined with a run-time buffer base.
+  auto step = [&](const int tile, const int buf) {
     const int k0 = tile * kKTile;
-    const int buf = tile & 1;
     __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
     if (tile + 1 < n_tiles) {
       store_tile(buf ^ 1);
@@ -615,6 +617,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
           V8, u32x4{dspk[nb][base], dspk[nb][base + 1], dspk[nb][base + 2], dspk[nb][base + 3]});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dq[db] = T::mfma(trl.template tr<V8>(Ks[buf], db, t2), sb, dq[db]);
+    }
+  };
+  if constexpr (MOD == kModAll) {  // (the bias loads' registers leave no room for two copies)
+    for (int tile = 0; tile < n_tiles; ++tile) step(tile, tile & 1);
+  } else {
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      step(tile, 0);
+      if (tile + 1 < n_tiles) step(tile + 1, 1);
     }
   }
   if (my_q < a.s_q) {
