@@ -24,6 +24,10 @@
 //    LDS once per workgroup through registers, double-buffered, and shared by
 //    the waves; under the causal mask, tiles entirely above the diagonal are
 //    never loaded, and diagonal tiles are masked element-wise;
+//  * without score modifiers no per-tile row max is taken: the weights use
+//    the running max as it stands (started at the row's key-0 score) and are
+//    rescaled by a power of two only when a tile's weights outgrow 2^8; an
+//    fp32 overflow sends the workgroup back over its rows on the exact path;
 //  * workgroups are issued longest-first for the causal mask, and heads are
 //    remapped so that all query blocks of a head (and the query heads of a
 //    GQA group) run on the same XCD and share its L2.
@@ -165,150 +169,230 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     for (int i = 0; i < KCH; ++i) *(u32x4*)(&Vs[buf][vdst2[i]]) = vreg2[i];
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(kBN);
-  }
+  // The tile loop. fast (no modifiers only): the weights of a tile are taken
+  // against the running max without its row max; returns true when a weight
+  // overflowed, and the rows must be redone with fast = false.
+  auto run = [&](const bool fast) -> bool {
+    bool bad = false;
+    if (n_tiles > 0) {
+      load_tile(0);
+      store_tile(0);
+      if (n_tiles > 1) load_tile(kBN);
+    }
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int k0 = tile * kBN;
-    const int buf = tile & 1;
-    __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
-    if (tile + 1 < n_tiles) {
-      store_tile(buf ^ 1);
-      if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
-    }
-    if (CAUSAL && k0 > q0 + 31 + L.off) continue;  // every key of this tile is above this wave's rows
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int k0 = tile * kBN;
+      const int buf = tile & 1;
+      __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
+      if (tile + 1 < n_tiles) {
+        store_tile(buf ^ 1);
+        if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
+      }
+      if (CAUSAL && k0 > q0 + 31 + L.off) continue;  // every key of this tile is above this wave's rows
 
-    // S^T = K Q^T for the 64 keys of the tile.
-    f32x16 sacc[NSB];
+      // S^T = K Q^T for the 64 keys of the tile.
+      f32x16 sacc[NSB];
 #pragma unroll
-    for (int nb = 0; nb < NSB; ++nb) {
-      sacc[nb] = f32x16{};
+      for (int nb = 0; nb < NSB; ++nb) {
+        sacc[nb] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        const V8 kf = *(const V8*)(&Ks[buf][(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
-        sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
+        for (int t = 0; t < NKS; ++t) {
+          const V8 kf = *(const V8*)(&Ks[buf][(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
+          sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
+        }
       }
-    }
-    if constexpr (MOD == kModNone) {
-      // Schedule: the K operand reads run kLook MFMAs ahead (the default
-      // schedule read each operand just before its MFMA). 1.5 % on the hd128
-      // forward, no extra spills.
-      __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // LDS reads
+      if constexpr (MOD == kModNone) {
+        // Schedule: the K operand reads run kLook MFMAs ahead (the default
+        // schedule read each operand just before its MFMA). 1.5 % on the hd128
+        // forward, no extra spills.
+        __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // LDS reads
 #pragma unroll
-      for (int i = 0; i < NSB * NKS - kLook; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        for (int i = 0; i < NSB * NKS - kLook; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
-    }
-    if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
+      if (MOD == kModNone && fast && tile == 0) {
+        // Starting max: this row's score against key 0 (unmasked), which every
+        // row that sees any key sees (a row's visible keys are a prefix). An
+        // actual score is a lower bound of the row max, so no weight
+        // underflows for want of a larger one; and a row whose max is key 0
+        // (causal row 0) gets the weight exp2(0) = 1 for it, as with an exact
+        // max. Key 0 is accumulator register 0 of the lower half-wave.
+        const float s_key0 = sacc[0][0];
+        const float other = __shfl_xor(s_key0, 32, 64);
+        m_run = (h ? other : s_key0) * sc;
+      }
+      if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
 #pragma unroll
-      for (int nb = 0; nb < NSB; ++nb)
+        for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
-          const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
+            const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
-            sacc[nb][4 * q4 + e] = fmaf(sacc[nb][4 * q4 + e], sl2, fmaf(bv[e], kLog2e, -slope2 * dist));
+            for (int e = 0; e < 4; ++e) {
+              const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
+              sacc[nb][4 * q4 + e] = fmaf(sacc[nb][4 * q4 + e], sl2, fmaf(bv[e], kLog2e, -slope2 * dist));
+            }
+          }
+      }
+      // Causal / key-length mask (only tiles that cross the diagonal or lk).
+      const bool need_mask = (k0 + kBN > L.lk) || (CAUSAL && k0 + kBN - 1 > q0 + L.off);
+      if (need_mask) {
+        // Key k0 + c (c = nb * 32 + acc_row(r, h)) is visible iff k0 + c <= last,
+        // the last key this row sees; one compare against a constant per score.
+        const int last = CAUSAL ? min(L.lk - 1, my_q + L.off) : L.lk - 1;
+        const int lim = last - k0 - 4 * h;
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (nb * 32 + acc_row(r, 0) > lim) sacc[nb][r] = -INFINITY;
+      }
+      uint32_t pk[NSB][8];
+      float lsum0 = 0.f, lsum1 = 0.f;
+      if (MOD == kModNone && fast) {
+        // Weights against the running max as it stands: no row max per tile.
+        // The max only grows when a weight says so: every weight is >= 0, so
+        // a lane sum <= 2^8 bounds each one by 2^8 (as the stale max of the
+        // exact path does). Otherwise (rare) the lane's weights are scaled by
+        // a power of two that brings their max into [1/2, 1), exactly, with O
+        // and l; a weight that overflowed fp32 cannot be scaled, and the
+        // workgroup redoes the rows on the exact path.
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            sacc[nb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sc, -m_run));
+            sacc[nb][r + 1] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -m_run));
+            lsum0 += sacc[nb][r];
+            lsum1 += sacc[nb][r + 1];
+          }
+        if (__any(!(lsum0 + lsum1 <= 256.f))) {
+          float mx = 0.f;
+#pragma unroll
+          for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+          mx = wave_max_halves(mx);
+          bad = bad || __any(!(mx <= 3.0e38f));
+          const int e = mx > 1.f && mx <= 3.0e38f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+          m_run += (float)e;
+          l_run = __builtin_amdgcn_ldexpf(l_run, -e);
+          lsum0 = __builtin_amdgcn_ldexpf(lsum0, -e);
+          lsum1 = __builtin_amdgcn_ldexpf(lsum1, -e);
+#pragma unroll
+          for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[nb][r] = __builtin_amdgcn_ldexpf(sacc[nb][r], -e);
+#pragma unroll
+          for (int i = 0; i < NDB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] = __builtin_amdgcn_ldexpf(oacc[i][r], -e);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) pk[nb][r / 2] = pack2<T>(sacc[nb][r], sacc[nb][r + 1]);
+      } else {
+        // Online softmax. The running max is only moved (and O, l rescaled) when
+        // some row's max grew by more than 8 (log2 units): with a stale max the
+        // weights stay below 2^8, and the final O / l and LSE are unchanged.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+        mx = wave_max_halves(mx) * sc;
+        if (__any(mx > m_run + 8.f)) {
+          const float m_new = fmaxf(m_run, mx);
+          // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < NDB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        }
+
+        // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand
+        // (m = -inf only while every score of the row is -inf: P = 0).
+        const float msub = m_run == -INFINITY ? 0.f : m_run;
+        // Dropout words of this row for the tile's key groups (nb, q4): the four
+        // lanes of a query quad draw one block each (q4 = lane & 3) and trade words.
+        u32x4 dwq[NSB];
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb) {
+          dwq[nb] = u32x4{0u, 0u, 0u, 0u};
+          if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
+            const u32x4 w = drop_words((uint32_t)(k0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
+                                       drop_slot, a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
+            dwq[nb] = quad_transpose(w, lane);
           }
         }
-    }
-    // Causal / key-length mask (only tiles that cross the diagonal or lk).
-    const bool need_mask = (k0 + kBN > L.lk) || (CAUSAL && k0 + kBN - 1 > q0 + L.off);
-    if (need_mask) {
 #pragma unroll
-      for (int nb = 0; nb < NSB; ++nb)
+        for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= L.lk || (CAUSAL && key > my_q + L.off)) sacc[nb][r] = -INFINITY;
-        }
-    }
-    // Online softmax. The running max is only moved (and O, l rescaled) when
-    // some row's max grew by more than 8 (log2 units): with a stale max the
-    // weights stay below 2^8, and the final O / l and LSE are unchanged.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < NSB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-    mx = wave_max_halves(mx) * sc;
-    if (__any(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-
-    // P = exp2(S * scale * log2e - m), packed to 16 bits as the B operand
-    // (m = -inf only while every score of the row is -inf: P = 0).
-    const float msub = m_run == -INFINITY ? 0.f : m_run;
-    // Dropout words of this row for the tile's key groups (nb, q4): the four
-    // lanes of a query quad draw one block each (q4 = lane & 3) and trade words.
-    u32x4 dwq[NSB];
-#pragma unroll
-    for (int nb = 0; nb < NSB; ++nb) {
-      dwq[nb] = u32x4{0u, 0u, 0u, 0u};
-      if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
-        const u32x4 w = drop_words((uint32_t)(k0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
-                                   drop_slot, a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
-        dwq[nb] = quad_transpose(w, lane);
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sc, -msub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
+            lsum0 += p0;  // the row sum uses the undropped weights
+            lsum1 += p1;
+            if (MOD >= kModDrop) {
+              // Dropout word of this row for the 4-key group of r (0, i.e. every
+              // byte kept, without dropout); byte r % 4 decides key r.
+              const uint32_t dw = dwq[nb][r / 4];
+              const bool k_0 = drop_keep(dw, r % 4, a.mod.drop_k8);
+              const bool k_1 = drop_keep(dw, (r + 1) % 4, a.mod.drop_k8);
+              pk[nb][r / 2] = pack2<T>(k_0 ? p0 : 0.f, k_1 ? p1 : 0.f);
+            } else {
+              pk[nb][r / 2] = pack2<T>(p0, p1);
+            }
+          }
       }
-    }
-    uint32_t pk[NSB][8];
-    float lsum0 = 0.f, lsum1 = 0.f;
+      l_run += lsum0 + lsum1;
+
+      // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
-    for (int nb = 0; nb < NSB; ++nb)
+      for (int t2 = 0; t2 < kBN / 16; ++t2) {
+        const int nb = t2 / 2, base = 4 * (t2 % 2);
+        u32x4 bw = u32x4{pk[nb][base], pk[nb][base + 1], pk[nb][base + 2], pk[nb][base + 3]};
+        const V8 pb = __builtin_bit_cast(V8, bw);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sc, -msub));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sc, -msub));
-        lsum0 += p0;  // the row sum uses the undropped weights
-        lsum1 += p1;
-        if (MOD >= kModDrop) {
-          // Dropout word of this row for the 4-key group of r (0, i.e. every
-          // byte kept, without dropout); byte r % 4 decides key r.
-          const uint32_t dw = dwq[nb][r / 4];
-          const bool k_0 = drop_keep(dw, r % 4, a.mod.drop_k8);
-          const bool k_1 = drop_keep(dw, (r + 1) % 4, a.mod.drop_k8);
-          pk[nb][r / 2] = pack2<T>(k_0 ? p0 : 0.f, k_1 ? p1 : 0.f);
-        } else {
-          pk[nb][r / 2] = pack2<T>(p0, p1);
+        for (int db = 0; db < NDB; ++db) {
+          const V8 va = sl.template tr<V8>(Vs[buf], db, t2);
+          oacc[db] = T::mfma(va, pb, oacc[db]);
         }
       }
-    l_run += lsum0 + lsum1;
-
-    // O^T += V^T P^T, 16 keys per step.
+      if constexpr (MOD == kModNone) {  // the same for the V^T reads, two per MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 1);
 #pragma unroll
-    for (int t2 = 0; t2 < kBN / 16; ++t2) {
-      const int nb = t2 / 2, base = 4 * (t2 % 2);
-      u32x4 bw = u32x4{pk[nb][base], pk[nb][base + 1], pk[nb][base + 2], pk[nb][base + 3]};
-      const V8 pb = __builtin_bit_cast(V8, bw);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const V8 va = sl.template tr<V8>(Vs[buf], db, t2);
-        oacc[db] = T::mfma(va, pb, oacc[db]);
+        for (int i = 0; i < (kBN / 16) * NDB - kLook; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kLook, 1);
       }
     }
-    if constexpr (MOD == kModNone) {  // the same for the V^T reads, two per MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 1);
+    return bad;
+  };
+  if constexpr (MOD == kModNone) {
+    __shared__ int redo;
+    if (tid == 0) redo = 0;  // the loop's barriers order this before any wave sets it
+    if (run(true) && lane == 0) redo = 1;
+    __syncthreads();
+    if (redo) {  // (uniform over the workgroup)
 #pragma unroll
-      for (int i = 0; i < (kBN / 16) * NDB - kLook; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kLook, 1);
+      for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      run(false);
     }
+  } else {
+    run(false);
   }
 
   // Epilogue: O = O_acc / l, LSE = ln l + m. Rows past lq, and rows that see
