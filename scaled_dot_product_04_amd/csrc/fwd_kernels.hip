@@ -54,23 +54,29 @@ __device__ __forceinline__ void map_block(int id, int n_qblk, int bh_total, int 
 
 // NW waves per workgroup, 32 query rows per wave. MOD: score modifiers added
 // to the scaled scores (kModAlibi: ALiBi slopes only; kModDrop: dropout and
-// ALiBi; kModAll: also a bias tensor).
-template <typename T, int D, bool CAUSAL, int NW, int MOD>
+// ALiBi; kModAll: also a bias tensor). KS = 2 splits the keys of each staged
+// tile between two groups of NW / 2 waves that own the same query rows (for
+// grids too small to fill the GPU: it halves the chain of tiles that the
+// longest workgroup walks); the groups merge their (m, l, O) at the end.
+template <typename T, int D, bool CAUSAL, int NW, int MOD, int KS>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, int n_qblk) {
   typedef typename T::elem E;
   typedef typename T::vec8 V8;
+  static_assert(KS == 1 || (KS == 2 && MOD == kModNone && NW == 8), "key split: 8 waves, no modifiers");
   constexpr int NT = 64 * NW;    // threads
-  constexpr int BM = 32 * NW;    // query rows per workgroup
+  constexpr int RW = NW / KS;    // waves per key group, each with its own 32 query rows
+  constexpr int BM = 32 * RW;    // query rows per workgroup
   // Keys per K/V tile: 128 at d = 128 (halves the per-tile barrier, row-max
   // reduction and loop overhead; 246 VGPRs, 135 KB LDS at 8 waves), 64 at
   // d = 64 (keeps three waves per SIMD) and with score modifiers (their
   // registers would not fit beside 128-key score tiles).
-  constexpr int kBN = (D == 128 && MOD == kModNone && NW == 8) ? 128 : 64;
+  constexpr int kBN = (KS == 2 || (D == 128 && MOD == kModNone && NW == 8)) ? 128 : 64;
+  constexpr int GBN = kBN / KS;  // keys of the tile that one wave takes
   constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
   constexpr int kLook = 4;       // MFMAs by which operand reads run ahead
   constexpr int NKS = D / 16;    // 16-wide contraction steps over d
   constexpr int NDB = D / 32;    // 32-wide output blocks over d
-  constexpr int NSB = kBN / 32;  // 32-key score blocks per tile
+  constexpr int NSB = GBN / 32;  // 32-key score blocks per tile and wave
   constexpr int CH = D / 8;                    // 16-byte chunks per K or V row
   constexpr int KCH = kBN * CH / NT;           // K (and V) chunks staged per thread
   static_assert(KCH * NT == kBN * CH, "tile / thread mismatch");
@@ -83,11 +89,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
+  const int grp = wave / RW, rw = wave - grp * RW;  // key group, row wave
+  const int kg = grp * GBN;                         // the group's keys in a tile
   int qb, bi, hq;
   map_block(blockIdx.x, n_qblk, a.b * a.h_q, a.h_q, a.h_q / a.h_kv, qb, bi, hq);
   const int g = hq / (a.h_q / a.h_kv);
   const int qblk0 = qb * BM;
-  const int q0 = qblk0 + wave * 32;
+  const int q0 = qblk0 + rw * 32;
   const int my_q = q0 + j;
   const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
 
@@ -188,7 +196,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         store_tile(buf ^ 1);
         if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
       }
-      if (CAUSAL && k0 > q0 + 31 + L.off) continue;  // every key of this tile is above this wave's rows
+      const int kg0 = k0 + kg;  // first key of this wave's part of the tile
+      if (CAUSAL && kg0 > q0 + 31 + L.off) continue;  // every key of it is above this wave's rows
 
       // S^T = K Q^T for the 64 keys of the tile.
       f32x16 sacc[NSB];
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         sacc[nb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NKS; ++t) {
-          const V8 kf = *(const V8*)(&Ks[buf][(nb * 32 + j) * KSTR + 16 * t + 8 * h]);
+          const V8 kf = *(const V8*)(&Ks[buf][(kg + nb * 32 + j) * KSTR + 16 * t + 8 * h]);
           sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
         }
       }
@@ -214,12 +223,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
       }
       if (MOD == kModNone && fast && tile == 0) {
-        // Starting max: this row's score against key 0 (unmasked), which every
-        // row that sees any key sees (a row's visible keys are a prefix). An
-        // actual score is a lower bound of the row max, so no weight
-        // underflows for want of a larger one; and a row whose max is key 0
-        // (causal row 0) gets the weight exp2(0) = 1 for it, as with an exact
-        // max. Key 0 is accumulator register 0 of the lower half-wave.
+        // Starting max: this row's score against the wave's first key kg
+        // (unmasked; key 0 without a key split). A row's visible keys are a
+        // prefix, so a row that sees any key this wave takes sees that one,
+        // and an actual score is a lower bound of the row max: no weight
+        // underflows for want of a larger one. (Rows that see none of the
+        // wave's keys get no weight at all.) A row whose max is key 0, like
+        // causal row 0, gets the weight exp2(0) = 1 for it, as with an exact
+        // max. The first key is accumulator register 0 of the lower half-wave.
         const float s_key0 = sacc[0][0];
         const float other = __shfl_xor(s_key0, 32, 64);
         m_run = (h ? other : s_key0) * sc;
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int key0 = k0 + nb * 32 + 8 * q4 + 4 * h;
+            const int key0 = kg0 + nb * 32 + 8 * q4 + 4 * h;
             const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -239,12 +250,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
           }
       }
       // Causal / key-length mask (only tiles that cross the diagonal or lk).
-      const bool need_mask = (k0 + kBN > L.lk) || (CAUSAL && k0 + kBN - 1 > q0 + L.off);
+      const bool need_mask = (kg0 + GBN > L.lk) || (CAUSAL && kg0 + GBN - 1 > q0 + L.off);
       if (need_mask) {
         // Key k0 + c (c = nb * 32 + acc_row(r, h)) is visible iff k0 + c <= last,
         // the last key this row sees; one compare against a constant per score.
         const int last = CAUSAL ? min(L.lk - 1, my_q + L.off) : L.lk - 1;
-        const int lim = last - k0 - 4 * h;
+        const int lim = last - kg0 - 4 * h;
 #pragma unroll
         for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         for (int nb = 0; nb < NSB; ++nb) {
           dwq[nb] = u32x4{0u, 0u, 0u, 0u};
           if (MOD >= kModDrop && a.mod.drop_k8 < 256) {
-            const u32x4 w = drop_words((uint32_t)(k0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
+            const u32x4 w = drop_words((uint32_t)(kg0 + nb * 32 + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)my_q >> 2,
                                        drop_slot, a.mod.offset, a.mod.seed_lo, a.mod.seed_hi);
             dwq[nb] = quad_transpose(w, lane);
           }
@@ -357,20 +368,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
 
       // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
-      for (int t2 = 0; t2 < kBN / 16; ++t2) {
+      for (int t2 = 0; t2 < GBN / 16; ++t2) {
         const int nb = t2 / 2, base = 4 * (t2 % 2);
         u32x4 bw = u32x4{pk[nb][base], pk[nb][base + 1], pk[nb][base + 2], pk[nb][base + 3]};
         const V8 pb = __builtin_bit_cast(V8, bw);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const V8 va = sl.template tr<V8>(Vs[buf], db, t2);
+          const V8 va = sl.template tr<V8>(Vs[buf] + kg * D, db, t2);
           oacc[db] = T::mfma(va, pb, oacc[db]);
         }
       }
       if constexpr (MOD == kModNone) {  // the same for the V^T reads, two per MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 1);
 #pragma unroll
-        for (int i = 0; i < (kBN / 16) * NDB - kLook; ++i) {
+        for (int i = 0; i < (GBN / 16) * NDB - kLook; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
@@ -393,6 +404,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     }
   } else {
     run(false);
+  }
+  if constexpr (KS == 2) {
+    // Group 1 hands its running (O, m, l) to the group-0 wave with the same
+    // rows through LDS (the K tile buffers, free once every wave is done):
+    // m = max(m0, m1), O = O0 e^(m0 - m) + O1 e^(m1 - m), l likewise.
+    constexpr int XS = NDB * 16 + 2;  // floats per lane
+    static_assert(RW * 64 * XS * sizeof(float) <= sizeof(Ks), "merge buffer");
+    float* const xp = reinterpret_cast<float*>(&Ks[0][0]) + (rw * 64 + lane) * XS;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xp[i * 16 + r] = oacc[i][r];
+      xp[NDB * 16] = m_run;
+      xp[NDB * 16 + 1] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xp[NDB * 16], l1 = xp[NDB * 16 + 1];
+    const float m_new = fmaxf(m_run, m1);
+    // A group that saw no key of these rows has m = -inf, O = l = 0: weight 0.
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] = oacc[i][r] * a0 + xp[i * 16 + r] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m_new;
   }
 
   // Epilogue: O = O_acc / l, LSE = ln l + m. Rows past lq, and rows that see
@@ -512,16 +553,26 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
   }
 }
 
-template <typename T, int D, int NW, int MOD>
+template <typename T, int D, int NW, int MOD, int KS = 1>
 hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
-  const int bm = 32 * NW;
+  const int bm = 32 * NW / KS;
   const int n_qblk = (a.s_q + bm - 1) / bm;
   const dim3 grid(n_qblk * a.b * a.h_q), block(64 * NW);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW, MOD>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW, MOD, KS>), grid, block, 0, stream, a, n_qblk);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW, MOD>), grid, block, 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW, MOD, KS>), grid, block, 0, stream, a, n_qblk);
   return hipGetLastError();
+}
+
+// The d = 64 forward splits each tile's keys between two wave groups when
+// its 128-row blocks are too few to fill the GPU twice over and the rows are
+// long enough for the chain of tiles to matter (the GPT-2-like b4 h12 s1024
+// shape has 384 blocks of up to 16 tiles).
+constexpr int kKeySplitMaxBlocks = 1024;
+inline bool use_key_split(const FwdArgs& a) {
+  const int64_t blocks = (int64_t)((a.s_q + 127) / 128) * a.b * a.h_q;
+  return blocks <= kKeySplitMaxBlocks && a.s_kv >= 256;
 }
 
 template <typename T, int D, int NW>
@@ -530,7 +581,11 @@ hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
     case kModAll: return launch_mfma_dm<T, D, NW, kModAll>(a, stream);
     case kModDrop: return launch_mfma_dm<T, D, NW, kModDrop>(a, stream);
     case kModAlibi: return launch_mfma_dm<T, D, NW, kModAlibi>(a, stream);
-    default: return launch_mfma_dm<T, D, NW, kModNone>(a, stream);
+    default:
+      if constexpr (D == 64) {
+        if (use_key_split(a)) return launch_mfma_dm<T, D, 8, kModNone, 2>(a, stream);
+      }
+      return launch_mfma_dm<T, D, NW, kModNone>(a, stream);
   }
 }
 

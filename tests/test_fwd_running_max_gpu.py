@@ -59,13 +59,18 @@ def test_scores_climb_along_keys(dtype, d, causal):
     _check(w, _structured(w, lambda j: (j // 16) / 16.0 - 1.0))
 
 
-@pytest.mark.parametrize("dtype,s", [("bf16", 300), ("f16", 300), ("bf16", 1030)])
+@pytest.mark.parametrize("dtype,s,d", [("bf16", 300, 128), ("f16", 300, 128), ("bf16", 1030, 128),
+                                       ("f16", 300, 64)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_weight_overflow_redoes_rows(dtype, s, causal):
-    """Key 0 scores 0; every other key scores 9 * 128 / sqrt(128) = 101.8 (146.9 in log2
-    units), past fp32's exp2 range when taken against key 0's score."""
-    w = Workload("ovf", 2, 2, 1, s, s, 128, dtype, dtype, causal, 1 / math.sqrt(128), "bhsd", 32)
-    _check(w, _structured(w, lambda j: 0.0 if j == 0 else 3.0))
+def test_weight_overflow_redoes_rows(dtype, s, d, causal):
+    """Key 0 scores 0; every other key scores 3 c d / sqrt(d) with c = 3 at d = 128 (101.8,
+    146.9 in log2 units) and c = 4.5 at d = 64 (108, 155.8 in log2 units): past fp32's exp2
+    range when taken against key 0's score. (At d = 64 the second key group of the split
+    forward starts from key 64's score and overflows nothing; the first group's overflow
+    sends the whole workgroup back.)"""
+    w = Workload("ovf", 2, 2, 1, s, s, d, dtype, dtype, causal, 1 / math.sqrt(d), "bhsd", 32)
+    c = 3.0 if d == 128 else 4.5
+    _check(w, _structured(w, lambda j: 0.0 if j == 0 else c))
 
 
 def test_overflow_in_some_heads_only():
