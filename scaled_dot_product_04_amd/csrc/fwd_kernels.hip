@@ -408,10 +408,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   if constexpr (KS == 2) {
     // Group 1 hands its running (O, m, l) to the group-0 wave with the same
     // rows through LDS (the K tile buffers, free once every wave is done):
-    // m = max(m0, m1), O = O0 e^(m0 - m) + O1 e^(m1 - m), l likewise.
-    constexpr int XS = NDB * 16 + 2;  // floats per lane
+    // m = max(m0, m1), O = O0 e^(m0 - m) + O1 e^(m1 - m), l likewise. A group
+    // whose row total l is 0 saw no key of that row and adds nothing; its m
+    // may be a masked key's score (the starting max), so it is left out of
+    // the max too.
+    constexpr int XS = NDB * 16 + 3;  // floats per lane
     static_assert(RW * 64 * XS * sizeof(float) <= sizeof(Ks), "merge buffer");
     float* const xp = reinterpret_cast<float*>(&Ks[0][0]) + (rw * 64 + lane) * XS;
+    const float lt = wave_sum_halves(l_run);  // this group's row total
     __syncthreads();
     if (grp == 1) {
 #pragma unroll
@@ -420,14 +424,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         for (int r = 0; r < 16; ++r) xp[i * 16 + r] = oacc[i][r];
       xp[NDB * 16] = m_run;
       xp[NDB * 16 + 1] = l_run;
+      xp[NDB * 16 + 2] = lt;
     }
     __syncthreads();
     if (grp == 1) return;
-    const float m1 = xp[NDB * 16], l1 = xp[NDB * 16 + 1];
-    const float m_new = fmaxf(m_run, m1);
-    // A group that saw no key of these rows has m = -inf, O = l = 0: weight 0.
-    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
+    const float m1 = xp[NDB * 16], l1 = xp[NDB * 16 + 1], lt1 = xp[NDB * 16 + 2];
+    const float m_new = fmaxf(lt == 0.f ? -INFINITY : m_run, lt1 == 0.f ? -INFINITY : m1);
+    const float a0 = lt == 0.f ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float a1 = lt1 == 0.f ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll

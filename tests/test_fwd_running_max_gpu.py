@@ -82,3 +82,23 @@ def test_overflow_in_some_heads_only():
     ins["q"][:, 1].copy_(rnd["q"][:, 1])
     ins["k"][:, 1].copy_(rnd["k"][:, 1])
     _check(w, ins)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,skv", [(1, 300), (77, 1000), (300, 257), (130, 4100)])
+def test_key_split_shapes(sq, skv, causal):
+    """d = 64 shapes that take the two-group key split (few row blocks, >= 256 keys): a
+    single query row, key counts that end mid-tile and mid-group, s_q != s_kv (top-left
+    causal: rows see keys 0..i, so the second group sees nothing for the first rows)."""
+    w = Workload("ksplit", 2, 3, 1, sq, skv, 64, "f16", "f16", causal, 0.125, "bshd", 34 + sq)
+    _check(w, sdpa_inputs.make_inputs(w, with_grad=False))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_key_split_group_without_visible_keys(dtype):
+    """Causal d = 64 key split: rows 0..63 see none of the second group's keys, whose first key
+    (key 64) scores 155.8 log2 units above every key those rows see. That group's starting max
+    is then a masked key's score, and its empty partial must not move the merged max (it would
+    scale the first group's weights to zero)."""
+    w = Workload("ksplit_empty", 1, 2, 2, 300, 300, 64, dtype, dtype, True, 0.125, "bshd", 35)
+    _check(w, _structured(w, lambda j: 4.5 if 64 <= j < 128 else 0.0))
