@@ -35,7 +35,10 @@ namespace {
 
 constexpr int kKvBlock = 256;  // keys per dK/dV workgroup (8 waves x 32)
 constexpr int kQTile = 32;     // query rows per dK/dV inner step
-constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
+// Waves (of 32 query rows) per dQ workgroup: at d = 128, 8 waves (one
+// workgroup per CU) share each K/V tile staging; at d = 64 a 32-key tile is
+// only 256 16-byte chunks, one per thread of 4 waves.
+constexpr int dq_waves(int d) { return d == 128 ? 8 : 4; }
 constexpr int kKTile = 32;     // keys per dQ inner step
 
 // Writes zeros to dK and dV (problems with no query rows).
@@ -435,9 +438,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split,
 // step t+1. K and V tiles are row-major in the bswz layout; the K^T operand of
 // dQ^T += K^T dS^T comes from the same K tile through ds_read_b64_tr_b16.
 template <typename T, int D, bool CAUSAL, int MOD>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
+__global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kernel(BwdArgs a, int n_qblk) {
   typedef typename T::vec8 V8;
-  typedef BswzTile<kKTile, D, 256> KvTile;
+  constexpr int kQBlock = 32 * dq_waves(D);
+  typedef BswzTile<kKTile, D, 64 * dq_waves(D)> KvTile;
   constexpr int NKS = D / 16, NDB = D / 32, NSB = kKTile / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile * D];
@@ -660,12 +664,12 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
   const int64_t rows = (int64_t)a.b * a.h_q * a.s_q;
   // dQ first: it also writes D = rowsum(dO * O), which dK/dV reads.
   if (timed) (void)hipEventRecord(te.ev[0], stream);
-  const int n_qblk = (a.s_q + kQBlock - 1) / kQBlock;
+  const int n_qblk = (a.s_q + 32 * dq_waves(D) - 1) / (32 * dq_waves(D));
   const dim3 g2(n_qblk * a.b * a.h_q);
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, MOD>), g2, dim3(64 * dq_waves(D)), 0, stream, a, n_qblk);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(256), 0, stream, a, n_qblk);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(64 * dq_waves(D)), 0, stream, a, n_qblk);
   if (timed) (void)hipEventRecord(te.ev[1], stream);
 
   const int n_split = choose_split(a.b, a.h_q, a.h_kv, a.s_kv);
