@@ -33,8 +33,9 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kNW = 4;       // waves per workgroup
-constexpr int kBM8 = 32 * kNW;
+// Waves (of 32 query rows) per workgroup: 8 at d = 256 (one workgroup per
+// CU, one K/V staging for eight waves), 4 at d = 128 (three per CU).
+constexpr int fp8_waves(int d) { return d == 256 ? 8 : 4; }
 constexpr int kBN8 = 64;     // keys per tile (one 64-deep MFMA step of P V)
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -56,13 +57,17 @@ __device__ __forceinline__ void transpose4x4_b8(const uint32_t in[4], uint32_t o
 }
 
 template <int D, bool CAUSAL>
-// Occupancy: two workgroups per CU at d = 256 (256 VGPRs, 2 x 74 KB LDS) and
-// three at d = 128 (168 VGPRs): a second (third) wave per SIMD hides the
-// softmax VALU work behind the other waves' MFMAs. The few VGPRs this spills
-// (staging offsets, reloaded from scratch a few times per key tile) cost far
-// less: same-box A/B at d = 256 (b4 h8 s8192), 2.28 ms with one wave per
-// SIMD, 1.86 ms with two.
-__global__ __launch_bounds__(64 * kNW, D == 256 ? 2 : 3) void fwd_fp8_kernel(FwdArgs a, int n_qblk) {
+// Occupancy: at d = 256 one 8-wave workgroup per CU (254 VGPRs, 74 KB LDS),
+// at d = 128 three 4-wave workgroups (168 VGPRs): a second (third) wave per
+// SIMD hides the softmax VALU work behind the other waves' MFMAs. At d = 256
+// the 8 waves share one K/V staging, which also halves each thread's staging
+// registers: two 4-wave workgroups per CU spilled 10 VGPRs and took 1.27 ms
+// on b4 h8 s8192, the 8-wave form 1.15 ms (same-box A/B; one wave per SIMD:
+// 2.28 ms). At d = 128, 8 waves (two per SIMD) lose to three 4-wave
+// workgroups: 0.44 vs 0.40 ms on b2 h16 s8192 causal.
+__global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_kernel(FwdArgs a, int n_qblk) {
+  constexpr int kNW = fp8_waves(D);
+  constexpr int kBM8 = 32 * kNW;
   constexpr int NT = 64 * kNW;
   constexpr int KSTR = D + 16;       // bytes per K row in LDS
   constexpr int VSTR = kBN8 + 16;    // bytes per transposed V row in LDS
@@ -286,8 +291,9 @@ __global__ __launch_bounds__(64 * kNW, D == 256 ? 2 : 3) void fwd_fp8_kernel(Fwd
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const int n_qblk = (a.s_q + kBM8 - 1) / kBM8;
-  const dim3 grid(n_qblk * a.b * a.h_q), block(64 * kNW);
+  const int bm = 32 * fp8_waves(D);
+  const int n_qblk = (a.s_q + bm - 1) / bm;
+  const dim3 grid(n_qblk * a.b * a.h_q), block(64 * fp8_waves(D));
   if (a.causal)
     hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), grid, block, 0, stream, a, n_qblk);
   else
