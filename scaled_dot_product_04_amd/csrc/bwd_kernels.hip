@@ -562,6 +562,17 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
         dp[nb] = T::mfma(va, df[t], dp[nb]);
       }
     }
+    if constexpr (MOD == kModNone) {
+      // Operand reads issued kLookQ MFMAs ahead of their MFMA.
+      constexpr int kLookQ = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLookQ, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NSB * NKS - kLookQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLookQ, 0);
+    }
     const bool need_mask = (k0 + kKTile > L.lk) || (CAUSAL && k0 + kKTile - 1 > q0 + L.off);
     if (need_mask) {
 #pragma unroll
@@ -621,6 +632,16 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
           V8, u32x4{dspk[nb][base], dspk[nb][base + 1], dspk[nb][base + 2], dspk[nb][base + 3]});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dq[db] = T::mfma(trl.template tr<V8>(Ks[buf], db, t2), sb, dq[db]);
+    }
+    if constexpr (MOD == kModNone) {  // the same for the K^T reads, two per MFMA
+      constexpr int kLookQ = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLookQ, 1);
+#pragma unroll
+      for (int i = 0; i < (kKTile / 16) * NDB - kLookQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLookQ, 1);
     }
   };
   if constexpr (MOD == kModAll) {  // (the bias loads' registers leave no room for two copies)
