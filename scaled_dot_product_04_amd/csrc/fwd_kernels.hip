@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
       const int kg0 = k0 + kg;  // first key of this wave's part of the tile
       if (CAUSAL && kg0 > q0 + 31 + L.off) continue;  // every key of it is above this wave's rows
 
-      // S^T = K Q^T for the 64 keys of the tile.
+      // S^T = K Q^T for this wave's GBN keys of the tile.
       f32x16 sacc[NSB];
 #pragma unroll
       for (int nb = 0; nb < NSB; ++nb) {
