@@ -287,9 +287,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
     }
     if (it + 1 < n_it) load_tile(it + 1);
     __syncthreads();  // this tile is in LDS
-    // (Tiles whose queries all precede this wave's keys are not skipped: the
-    // mask zeroes them, and a branch here would make the compiler copy the
-    // dK/dV accumulators between register files on every iteration.)
+    // Tiles whose queries all precede this wave's keys add nothing.
+    if (CAUSAL && q0 + kQTile - 1 + L.off < kw0) continue;
 
     // S = Q K^T and dP = dO V^T for 32 queries x this lane's key.
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -560,8 +559,7 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
       store_tile(buf ^ 1);
       if (tile + 2 < n_tiles) load_tile((tile + 2) * kKTile);
     }
-    // (Tiles above this wave's diagonal are masked, not skipped: a branch here
-    // makes the compiler copy the dQ accumulators between register files.)
+    if (CAUSAL && k0 > q0 + 31 + L.off) return;  // every key of the tile is above this wave's rows
     f32x16 s[NSB], dp[NSB];
 #pragma unroll
     for (int nb = 0; nb < NSB; ++nb) {
