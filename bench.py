@@ -94,6 +94,15 @@ TRAFFIC_RECORDS = {"bwd_dkdv": "profiles/hd128_causal_s8192_dkdv_hbm_traffic.jso
                    "bwd_dq": "profiles/hd128_causal_s8192_dq_hbm_traffic.json"}
 
 
+def kernel_sources(kernel: str) -> list:
+    """Files whose content decides what `kernel` does: its kernel file, the
+    shared device helpers, the argument layouts and variant levels, the build
+    flags. A traffic record counts only while all of them are unchanged."""
+    csrc = "scaled_dot_product_04_amd/csrc/"
+    main = csrc + ("bwd_kernels.hip" if kernel.startswith("bwd") else "fwd_kernels.hip")
+    return [main, csrc + "device_common.h", csrc + "sdpa_internal.h", "scaled_dot_product_04_amd/_build.py"]
+
+
 def sources_digest(paths) -> str:
     import hashlib
     h = hashlib.sha256()
@@ -112,7 +121,7 @@ def measured_traffic(kernel: str):
     if rec_path is None or not os.path.exists(os.path.join(ROOT, rec_path)):
         return None
     rec = json.load(open(os.path.join(ROOT, rec_path)))
-    if sources_digest(rec["sources"]) != rec["sources_sha256"]:
+    if rec.get("sources") != kernel_sources(kernel) or sources_digest(kernel_sources(kernel)) != rec["sources_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -147,9 +156,7 @@ def write_traffic_record(kernel: str, fetch_db: str, write_db: str, copy_fetch_d
     write_scale = gib_kib / per_dispatch(copy_write_db, "WRITE_SIZE")
     fetch = per_dispatch(fetch_db, "FETCH_SIZE", short)
     write = per_dispatch(write_db, "WRITE_SIZE", short)
-    sources = ["scaled_dot_product_04_amd/csrc/bwd_kernels.hip" if kernel.startswith("bwd")
-               else "scaled_dot_product_04_amd/csrc/fwd_kernels.hip",
-               "scaled_dot_product_04_amd/csrc/device_common.h", "scaled_dot_product_04_amd/_build.py"]
+    sources = kernel_sources(kernel)
     rec = {"kernel": short, "workload": "hd128_causal_s8192 (b2 h16 s8192 d128 bf16 causal BSHD)",
            "fetch_size_kib_per_launch": round(fetch, 1), "write_size_kib_per_launch": round(write, 1),
            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
@@ -239,6 +246,38 @@ def summarize_counters(dbs: list) -> str:
             out.append(f"| same, against the 2.4 GHz clock of the published peak | {100 * busy / 2.4e9:.1f} % |")
         out.append("")
     return "\n".join(out)
+
+
+def mfma_measured(sdpa, torch, hip, stream, sh) -> dict:
+    """Sustained dense MFMA rate (bf16 32x32x16, fp8 32x32x64) and the shader
+    clock while the matrix pipes are saturated, from the library's rate probe
+    (sdpa_mfma_probe): the measured denominator beside the published peaks."""
+    lib = sdpa.load_library()
+    blocks = 2 * 256  # two 4-wave workgroups per CU: two waves on every SIMD
+    stamps = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda:0")
+    out = {}
+    for name, code, flops_per in (("bf16", sdpa.SDPA_BF16, 32768.0), ("fp8", sdpa.SDPA_FP8_E4M3, 131072.0)):
+        iters = 40000 if name == "bf16" else 20000
+        best = None
+        for rep in range(4):  # the first launch warms up; keep the fastest of the rest
+            a, b = hip.event(), hip.event()
+            hip.record(a, sh)
+            st = lib.sdpa_mfma_probe(code, blocks, iters, ctypes.c_void_p(stamps.data_ptr()), sh)
+            hip.record(b, sh)
+            if st != 0:
+                raise RuntimeError(lib.sdpa_last_error().decode())
+            torch.cuda.synchronize()
+            ms = hip.ms(a, b)
+            if rep > 0 and (best is None or ms < best[0]):
+                s = stamps.view(blocks, 4).cpu().double()
+                cycles, real = s[:, 1] - s[:, 0], s[:, 3] - s[:, 2]
+                clk = float(statistics.median((cycles / real * 0.1).tolist()))  # GHz (real time counts at 100 MHz)
+                best = (ms, clk)
+        tf = blocks * 4 * iters * 8 * flops_per / (best[0] / 1e3) / 1e12
+        out[f"{name}_tflops"] = round(tf, 1)
+        out[f"{name}_clock_ghz"] = round(best[1], 3)
+    out["probe"] = "sdpa_mfma_probe: 512 workgroups x 4 waves, 8 independent MFMA chains per wave"
+    return out
 
 
 def fp8_forward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup: int, steps: int) -> dict:
@@ -456,6 +495,8 @@ def main() -> int:
     # The GPU clock ramps up over the first ~100 ms of sustained work: the
     # default warm-up (about 0.14 s of steps) times the kernels at steady clocks.
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-s", type=float, default=0.5,
+                    help="minimum seconds of warm-up steps before timing (on top of --warmup steps)")
     ap.add_argument("--seq", type=int, default=8192, help="sequence length of the hd128 sweep point (b = 16384/s)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads the CPU oracle baseline times (0 = skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the extra fp8 forward measurement")
@@ -548,8 +589,16 @@ def main() -> int:
         if ev is not None:
             lib.sdpa_set_timing_events(None, 0)
 
-    for _ in range(args.warmup):
+    # Warm up by count and by time: the clock ramps over the first ~100 ms of
+    # sustained work, so at least --warmup-s seconds of steps run first.
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < args.warmup or time.perf_counter() - t_w < args.warmup_s:
         step()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    warmup_s = time.perf_counter() - t_w
     events = [[hip.event().value for _ in range(5)] for _ in range(args.steps)]
     start, stop = hip.event(), hip.event()
     torch.cuda.synchronize()
@@ -588,6 +637,11 @@ def main() -> int:
     log(f"[bench] per-kernel median ms: " + ", ".join(f"{k}={v:.3f}" for k, v in med.items()))
     log(f"[bench] fwd {fwd_tflops:.1f} TFLOP/s ({100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% peak); "
         f"bwd {bwd_tflops:.1f}; fwd+bwd {value:.1f} ({100 * value / PEAK_BF16_TFLOPS:.1f}%)")
+
+    measured = mfma_measured(sdpa, torch, hip, stream, sh)
+    log(f"[bench] measured MFMA peak: {measured}")
+    measured["fwd_pct_of_measured_bf16"] = round(100 * fwd_tflops / measured["bf16_tflops"], 2)
+    measured["fwd_bwd_pct_of_measured_bf16"] = round(100 * value / measured["bf16_tflops"], 2)
 
     mods = None
     if not args.no_mods:
@@ -645,6 +699,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(warmup_s, 3),
+        "warmup_steps_run": n_w,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -662,6 +718,7 @@ def main() -> int:
         "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
+        "mfma_measured": measured,
         "fp8_forward": fp8,
         "fp8_hd128_forward_backward": fp8_train,
         "decode_forward": dec,

@@ -75,14 +75,6 @@ typedef enum {
 } sdpa_status_t;
 
 /*
- * Per-tensor fp8 factors (JAX attention codelab, step 10: per-tensor scaling
- * recipe). A real input value is x = e4m3(code) * descale_x. Inside the kernel
- * the softmax weights P (all in [0, 1]) are quantised as e4m3(P * scale_p)
- * before the second matmul and the result is multiplied back by descale_p.
- * The usual choice is scale_p = 448, descale_p = 1/448; scale_p must be <= 448
- * (SDPA_ERR_INVALID_ARGUMENT otherwise).
- */
-/*
  * Attention mask of sdpa_fwd_ex / sdpa_bwd_ex. The cuDNN 9 blog's SDPA node
  * call ("SDPA usage") lists the causal flag next to use_padding_mask with
  * per-batch seq_len_q / seq_len_kv; where the causal diagonal sits when the
@@ -137,6 +129,14 @@ typedef struct {
   uint32_t dropout_offset;
 } sdpa_score_mod_t;
 
+/*
+ * Per-tensor fp8 factors (JAX attention codelab, step 10: per-tensor scaling
+ * recipe). A real input value is x = e4m3(code) * descale_x. Inside the kernel
+ * the softmax weights P (all in [0, 1]) are quantised as e4m3(P * scale_p)
+ * before the second matmul and the result is multiplied back by descale_p.
+ * The usual choice is scale_p = 448, descale_p = 1/448; scale_p must be <= 448
+ * (SDPA_ERR_INVALID_ARGUMENT otherwise).
+ */
 typedef struct {
   float descale_q;
   float descale_k;
@@ -147,6 +147,15 @@ typedef struct {
 
 /*
  * Forward: O (and optionally LSE) from Q, K, V.
+ *
+ * Defined by the SDPA node call of the cuDNN 9 blog's "SDPA usage" section
+ * (q, k, v, attn_scale, is_inference, use_causal_mask in; o and stats out),
+ * computing the formula of the JAX attention codelab, step 1, with its step 7
+ * causal mask; the tensors are described by dims and strides and executed on
+ * caller pointers as in "Using cuDNN in Python" (graph build, then execute).
+ * Ownership: every pointer stays the caller's; nothing is allocated. Errors:
+ * invalid arguments and unsupported combinations are reported before any
+ * launch (status + sdpa_last_error()); a launch failure returns SDPA_ERR_HIP.
  *
  *   q       [b, h_q,  s_q,  d] in_dtype, strides q_stride
  *   k, v    [b, h_kv, s_kv, d] in_dtype, strides k_stride / v_stride
@@ -221,7 +230,9 @@ size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
 
 /*
  * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned
- * use). 0 is a valid answer only for empty problems. With dtype
+ * use): the workspace query of "Using cuDNN in Python" (get_workspace_size(),
+ * then a caller-allocated buffer handed to execute). Pure host arithmetic; no
+ * error state (invalid shapes give 0). 0 is a valid answer only for empty problems. With dtype
  * SDPA_FP8_E4M3 it is the size sdpa_bwd_fp8 needs (larger: it adds the bf16
  * copies of q, k, v and dout).
  */
@@ -230,6 +241,16 @@ size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
 
 /*
  * Backward: dQ, dK, dV of L = sum(O * dO).
+ *
+ * The cuDNN 9 blog shows the fused forward + backward ("SDPA performance",
+ * Figure 2) and a backward graph with the forward's flexibility ("SDPA as a
+ * cuDNN graph"); it does not print the backward's formulas, so this is the
+ * exact gradient of sdpa_fwd's result, recomputing the weights from the
+ * forward's stats (LSE), with dK / dV summed over each KV head's query-head
+ * group (JAX attention codelab, step 9). It runs in the execute(pointers,
+ * workspace) flow of "Using cuDNN in Python": the caller queries
+ * sdpa_bwd_workspace_size and owns the workspace. Errors as for sdpa_fwd;
+ * SDPA_ERR_WORKSPACE_TOO_SMALL when the workspace is short.
  *
  *   q, k, v, o, dout   as in sdpa_fwd (o is the forward's output, dout is dL/dO,
  *                      same layout rules); dtype BF16 or F16 for all of them.
@@ -321,6 +342,20 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The standard ALiBi slopes for h_q heads, written to host memory
+ * `slopes_host` (h_q floats; copy them to the device for
+ * sdpa_score_mod_t.alibi_slopes). The cuDNN 9 blog's SDPA node call ("SDPA
+ * usage") lists `use_alibi_mask` without its slopes; these are the ALiBi
+ * paper's (Press, Smith, Lewis, "Train Short, Test Long: Attention with
+ * Linear Biases"): for h_q a power of two the geometric sequence
+ * 2^(-8 (i + 1) / h_q), i = 0 .. h_q - 1; otherwise the slopes of the largest
+ * power of two n < h_q, followed by the first h_q - n even-indexed slopes
+ * (i = 0, 2, 4, ...) of the 2n-head sequence. Host-only: no device call.
+ * Returns SDPA_ERR_INVALID_ARGUMENT for h_q < 1 or slopes_host == NULL.
+ */
+sdpa_status_t sdpa_alibi_slopes(int h_q, float* slopes_host);
+
+/*
  * Timing hook (diagnostics only; GPU-time-only reporting as in the cuDNN 9
  * blog's "SDPA performance" section). Registers `n` caller-created HIP events
  * (n = 0 or events = NULL disables) that this thread's following sdpa_fwd /
@@ -335,10 +370,36 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
  */
 sdpa_status_t sdpa_set_timing_events(hipEvent_t* events, int n);
 
-/* Message describing this thread's most recent failed call ("" after a success). */
+/*
+ * Diagnostics: sustained matrix-core rate probe, the measured denominator
+ * beside the published dense peaks that the "% of MFMA peak" of the cuDNN 9
+ * blog's forward and forward + backward figures ("SDPA performance") is
+ * quoted against. Enqueues `blocks` workgroups of 4 waves on `stream`; every
+ * wave issues `iters` rounds of 8 independent MFMAs:
+ *   SDPA_BF16      v_mfma_f32_32x32x16_bf16          (32768 flops each)
+ *   SDPA_FP8_E4M3  v_mfma_scale_f32_32x32x64_f8f6f4  (131072 flops each)
+ * so one launch performs blocks * 4 * iters * 8 MFMAs; the caller times it
+ * (events on the stream). stamps: caller-owned device uint64 [4 * blocks],
+ * 16-byte aligned (written): per workgroup, the shader cycle counter at the
+ * start and end of its loop, then the 100 MHz real-time counter at the same
+ * two points (their ratio gives the shader clock under full matrix load).
+ * Errors: SDPA_ERR_INVALID_ARGUMENT for another dtype, blocks or iters < 1,
+ * or stamps NULL / misaligned; SDPA_ERR_HIP for a launch failure.
+ */
+sdpa_status_t sdpa_mfma_probe(sdpa_dtype_t dtype, int blocks, int iters, uint64_t* stamps, hipStream_t stream);
+
+/*
+ * Message describing this thread's most recent failed call ("" after a
+ * success): the programmatic last-error string of the cuDNN 9 blog's
+ * "Improved error reporting" section (cudnnGetLastErrorString). The string is
+ * owned by the library and valid until this thread's next call.
+ */
 const char* sdpa_last_error(void);
 
-/* Static name of a status code. */
+/*
+ * Static name of a status code (the categorised error codes of the cuDNN 9
+ * blog's "Improved error reporting"); "SDPA_ERR_UNKNOWN" for other values.
+ */
 const char* sdpa_status_string(sdpa_status_t status);
 
 #ifdef __cplusplus

@@ -16,5 +16,4 @@ from .sdpa_oracle import (  # noqa: F401
     fp8_e4m3_decode,
     fp8_e5m2_decode,
     philox4x32_10,
-    sdpa_flops,
 )

@@ -391,16 +391,10 @@ def fp8_dequantize(codes: np.ndarray, descale: float, fmt: str = "e4m3") -> np.n
     return fp8_e4m3_decode(codes) * float(descale)
 
 
-def sdpa_flops(b: int, h_q: int, s_q: int, s_kv: int, d: int, causal: bool) -> float:
-    """Counted forward flops 4*b*h*s_q*s_kv*d, halved under the causal mask."""
-    f = 4.0 * b * h_q * s_q * s_kv * d
-    return f / 2 if causal else f
-
-
 __all__ = [
     "attention_forward", "attention_backward", "attention_probs", "alibi_slopes", "philox4x32_10",
     "dropout_mask", "dropout_keep_threshold",
-    "fp8_e4m3_decode", "fp8_e5m2_decode", "fp8_dequantize", "sdpa_flops",
+    "fp8_e4m3_decode", "fp8_e5m2_decode", "fp8_dequantize",
 ]
 
 if __name__ == "__main__":  # pragma: no cover - tiny self-demo

@@ -101,6 +101,10 @@ def load_library() -> ctypes.CDLL:
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_status_string.argtypes = [i]
+    lib.sdpa_alibi_slopes.restype = ctypes.c_int
+    lib.sdpa_mfma_probe.restype = ctypes.c_int
+    lib.sdpa_mfma_probe.argtypes = [i, i, i, vp, vp]
+    lib.sdpa_alibi_slopes.argtypes = [i, ctypes.POINTER(ctypes.c_float)]
     lib.sdpa_set_timing_events.restype = ctypes.c_int
     lib.sdpa_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = lib
@@ -188,15 +192,11 @@ def _score_mod(bias, alibi_slopes, b, h_q, s_q, s_kv, device, dropout=None):
 
 
 def alibi_slopes(h: int, device="cuda") -> torch.Tensor:
-    """The ALiBi paper's per-head slopes (power-of-two head counts: 2^(-8 (i+1) / h);
-    otherwise the next lower power of two followed by every other slope of twice that)."""
-    def pow2(n):
-        return [2.0 ** (-8.0 * (i + 1) / n) for i in range(n)]
-    n = 1 << (h.bit_length() - 1)
-    out = pow2(n)
-    if n < h:
-        out += pow2(2 * n)[0::2][: h - n]
-    return torch.tensor(out, dtype=torch.float32, device=device)
+    """The standard ALiBi slopes of h heads as a float32 tensor on ``device``;
+    the library computes them (sdpa_alibi_slopes)."""
+    buf = (ctypes.c_float * h)()
+    _check(load_library().sdpa_alibi_slopes(int(h), buf))
+    return torch.tensor(list(buf), dtype=torch.float32, device=device)
 
 
 def fwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, dtype) -> int:

@@ -166,6 +166,31 @@ const char* sdpa_status_string(sdpa_status_t s) {
 
 const char* sdpa_last_error(void) { return g_last_error.c_str(); }
 
+sdpa_status_t sdpa_mfma_probe(sdpa_dtype_t dtype, int blocks, int iters, uint64_t* stamps, hipStream_t stream) {
+  g_last_error.clear();
+  if (dtype != SDPA_BF16 && dtype != SDPA_FP8_E4M3)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "mfma probe: dtype must be BF16 or FP8_E4M3 (got %d)", (int)dtype);
+  if (blocks < 1 || iters < 1)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "mfma probe: blocks=%d and iters=%d must be >= 1", blocks, iters);
+  if (stamps == nullptr || ((uintptr_t)stamps) % 16 != 0)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "mfma probe: stamps must be a non-NULL 16-byte aligned device pointer");
+  return hip_status(sdpa::launch_mfma_probe(dtype == SDPA_FP8_E4M3, blocks, iters, stamps, stream), "probe launch");
+}
+
+sdpa_status_t sdpa_alibi_slopes(int h_q, float* slopes_host) {
+  g_last_error.clear();
+  if (h_q < 1 || slopes_host == nullptr)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "alibi slopes: h_q=%d must be >= 1 and the output non-NULL", h_q);
+  int n = 1;  // largest power of two <= h_q
+  while (2 * n <= h_q) n *= 2;
+  // Geometric sequence of n heads: slope i = 2^(-8 (i + 1) / n).
+  for (int i = 0; i < n; ++i) slopes_host[i] = (float)exp2(-8.0 * (i + 1) / n);
+  // The remaining heads take the even-indexed slopes of the 2n-head sequence,
+  // 2^(-8 (2 k + 1) / (2 n)), k = 0, 1, ...
+  for (int k = 0; n + k < h_q; ++k) slopes_host[n + k] = (float)exp2(-8.0 * (2 * k + 1) / (2.0 * n));
+  return SDPA_OK;
+}
+
 sdpa_status_t sdpa_set_timing_events(hipEvent_t* events, int n) {
   g_last_error.clear();
   if (n < 0 || n > 8 || (n > 0 && events == nullptr))

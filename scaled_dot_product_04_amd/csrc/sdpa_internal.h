@@ -122,6 +122,10 @@ hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
 hipError_t launch_fp8_widen(const void* src, const Strides3& st, int b, int h, int s, int d, bool e5m2,
                             void* dst, hipStream_t stream);
 
+// Matrix-core rate probe (bf16 32x32x16 or fp8 32x32x64 MFMAs); stamps get
+// 4 uint64 per workgroup: shader cycles and real time at loop start and end.
+hipError_t launch_mfma_probe(bool fp8, int blocks, int iters, uint64_t* stamps, hipStream_t stream);
+
 // Workspace bytes the backward needs (see sdpa_bwd_workspace_size).
 size_t bwd_workspace_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d);
 

@@ -12,12 +12,14 @@ import sdpa_inputs
 from oracle import attention_backward, attention_forward, fp8_dequantize
 
 # Tolerances: max-abs error of the output vs the float64 oracle, per output
-# dtype; LSE |err| <= 1e-3 * max(1, |LSE|); gradients at twice the forward's.
-# An output stored in a 16-bit format cannot be closer to the exact value than
-# half a unit in the last place of that format, so the bound applied is
-# tol + half_ulp(|ref|): for |ref| below 4 (bf16) the extra term is at most
-# 0.008, but GQA/MQA gradients summed over many query heads reach 20+, where
-# bf16's own rounding (0.0625) exceeds any fixed absolute tolerance.
+# dtype (fp16 5e-3, bf16 2e-2, fp8 output 1e-1, fp32 1e-3); LSE
+# |err| <= 1e-3 * max(1, |LSE|); gradients at twice the forward's bound.
+# Forward outputs are held to the plain max-abs bound. A gradient stored in a
+# 16-bit format cannot be closer to the exact value than half a unit in the
+# last place of that format: GQA/MQA gradients summed over many query heads
+# reach |dV| ~ 20, where bf16's own half-ulp (0.0625) exceeds the 4e-2 bound.
+# Only for elements whose half-ulp reaches half the bound is the bound applied
+# to the error beyond that rounding; every other element gets the plain bound.
 TOL = {"f32": 1e-3, "f16": 5e-3, "bf16": 2e-2, "fp8": 1e-1}
 LSE_REL = 1e-3
 _MANT_BITS = {"f32": 23, "f16": 10, "bf16": 7}
@@ -72,10 +74,37 @@ def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
     return np.ldexp(1.0, (np.floor(np.log2(mag)) - _MANT_BITS[dtype] - 1).astype(np.int64))
 
 
-def excess_err(a: np.ndarray, ref: np.ndarray, dtype: str) -> float:
-    """max over elements of |a - ref| - half_ulp(ref): the error beyond the output format's rounding."""
+def bound_err(a: np.ndarray, ref: np.ndarray, dtype: str, tol: float) -> tuple[float, int]:
+    """(max over elements of |a - ref| - slack, number of elements given slack).
+
+    slack is half_ulp(ref) of the storage dtype where that reaches tol / 2 (the
+    element's own rounding would eat most of the bound), else 0: every other
+    element is held to the plain max-abs bound."""
     m = ~np.isnan(ref)
-    return float((np.abs(a[m] - ref[m]) - half_ulp(ref[m], dtype)).max()) if m.any() else 0.0
+    if not m.any():
+        return 0.0, 0
+    r, x = ref[m], a[m]
+    hu = half_ulp(r, dtype) if dtype in _MANT_BITS else np.zeros_like(r)
+    slack = np.where(hu >= tol / 2, hu, 0.0)
+    return float((np.abs(x - r) - slack).max()), int((slack > 0).sum())
+
+
+def check_out(a: np.ndarray, ref: np.ndarray, tol: float, *, grad_dtype: str | None = None, what: str = "") -> float:
+    """Assert the max-abs bound; returns the raw max-abs error.
+
+    Forward outputs (grad_dtype None) get the plain bound. Gradients pass their
+    storage dtype: elements whose half-ulp reaches tol / 2 are bounded beyond
+    that rounding (bound_err), and the count of such elements is printed."""
+    raw = max_abs(a, ref)
+    if grad_dtype is None:
+        say(f"    {what}max|err|={raw:.3e} relF={rel_fro(a, ref):.3e} (bound {tol:g})")
+        assert raw <= tol, (what, raw, tol)
+        return raw
+    err, n_relaxed = bound_err(a, ref, grad_dtype, tol)
+    say(f"    {what}max|err|={raw:.3e} bounded={err:.3e} relaxed_elems={n_relaxed} relF={rel_fro(a, ref):.3e} "
+        f"max|ref|={np.nanmax(np.abs(ref)) if ref.size else 0:.2f} (bound {tol:g})")
+    assert err <= tol, (what, raw, err, n_relaxed, tol)
+    return raw
 
 
 def max_abs(a: np.ndarray, b: np.ndarray) -> float:
@@ -91,5 +120,11 @@ def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray):
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    """||a - b||_F / ||b||_F over the non-NaN reference entries (0 when both are
+    zero, ||a - b||_F when only the reference is)."""
     m = ~np.isnan(b)
-    return float(np.linalg.norm(a[m] - b[m]) / np.linalg.norm(b[m]))
+    num = float(np.linalg.norm(a[m] - b[m]))
+    den = float(np.linalg.norm(b[m]))
+    if den == 0.0:
+        return num
+    return num / den

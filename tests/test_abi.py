@@ -246,3 +246,19 @@ def test_fp8_backward_workspace_holds_bf16_copies():
     assert fp8 % 16 == 0
     st, msg = _fwd_ex(tin=sdpa.SDPA_FP8_E5M2)  # e5m2 is a gradient format only
     assert st == 2 and "no forward kernel" in msg
+
+
+@pytest.mark.parametrize("h", [1, 2, 3, 8, 12, 16, 24, 31, 32, 64])
+def test_alibi_slopes_match_oracle(h):
+    """The library's host-side slope table equals the oracle's closed form
+    (the ALiBi paper's slopes) to float32 rounding."""
+    import numpy as np
+    from oracle import alibi_slopes as oracle_slopes
+    got = sdpa.alibi_slopes(h, device="cpu").double().numpy()
+    np.testing.assert_allclose(got, oracle_slopes(h), rtol=1e-7, atol=0)
+
+
+def test_alibi_slopes_rejects_bad_arguments():
+    lib = sdpa.load_library()
+    assert lib.sdpa_alibi_slopes(0, (ctypes.c_float * 1)()) == 1
+    assert lib.sdpa_alibi_slopes(4, None) == 1

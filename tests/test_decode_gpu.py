@@ -16,7 +16,7 @@ import scaled_dot_product_04_amd as sdpa
 import sdpa_inputs
 from oracle import attention_forward
 from sdpa_inputs import Workload
-from tests.parity import LSE_REL, TOL, excess_err, f64, max_abs, say, to_gpu
+from tests.parity import LSE_REL, TOL, check_out, f64, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -45,9 +45,7 @@ def _check(w, o, lse, o_ref, lse_ref, heads=None):
         for bi, hq in heads:
             sel[bi, hq] = True
         og, lg, o_ref, lse_ref = og[sel], lg[sel], o_ref[sel], lse_ref[sel]
-    exc = excess_err(og, o_ref, w.out_dtype)
-    say(f"    O: max|err|={max_abs(og, o_ref):.3e} beyond-rounding={exc:.3e}")
-    assert exc <= TOL[w.out_dtype], exc
+    check_out(og, o_ref, TOL[w.out_dtype], what="O: ")
     empty = np.isneginf(lse_ref)
     assert np.array_equal(np.isneginf(lg), empty)
     assert (og[empty] == 0).all()

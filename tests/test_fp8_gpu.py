@@ -13,7 +13,7 @@ import pytest
 
 import sdpa_inputs
 from sdpa_inputs import Workload
-from tests.parity import TOL, check_lse, excess_err, f64, gpu_fwd, max_abs, oracle_fwd, rel_fro, say, to_gpu
+from tests.parity import TOL, check_lse, check_out, f64, gpu_fwd, oracle_fwd, rel_fro, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,8 @@ def _check(w, o, lse, o_ref, lse_ref, rows=None):
     lg = lse.cpu().numpy()
     if rows is not None:
         og, lg = og[:, :, rows], lg[:, :, rows]
-    err, exc, rf = max_abs(og, o_ref), excess_err(og, o_ref, "bf16"), rel_fro(og, o_ref)
-    say(f"    fp8: max|dO|={err:.3e} beyond-rounding={exc:.3e} relF={rf:.3e} max|O|={np.nanmax(np.abs(o_ref)):.3f}")
-    assert exc <= TOL["fp8"], exc
+    check_out(og, o_ref, TOL["fp8"], what=f"fp8 O (max|O|={np.nanmax(np.abs(o_ref)):.3f}): ")
+    rf = rel_fro(og, o_ref)
     assert rf <= TOL["fp8"], rf
     check_lse(lg, lse_ref)
     return rf

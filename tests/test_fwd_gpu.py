@@ -12,8 +12,7 @@ import torch
 
 import sdpa_inputs
 from sdpa_inputs import Workload
-from tests.parity import (TOL, check_lse, excess_err, f64, gpu_fwd, max_abs, oracle_fwd, rel_fro,
-                          say, to_gpu)
+from tests.parity import TOL, check_lse, check_out, f64, gpu_fwd, oracle_fwd, rel_fro, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -24,10 +23,7 @@ def _run_full(w: Workload, check_lse_too=True):
     g = to_gpu(ins)
     o, lse = gpu_fwd(w, g)
     o_ref, lse_ref = oracle_fwd(w, ins)
-    err = max_abs(f64(o.cpu()), o_ref)
-    exc = excess_err(f64(o.cpu()), o_ref, w.out_dtype)
-    say(f"    max|dO|={err:.3e} beyond-rounding={exc:.3e} relF={rel_fro(f64(o.cpu()), o_ref):.3e}")
-    assert exc <= TOL[w.out_dtype], (err, exc)
+    check_out(f64(o.cpu()), o_ref, TOL[w.out_dtype], what="O: ")
     if check_lse_too:
         check_lse(lse.cpu().numpy(), lse_ref)
     return o, lse, ins
@@ -85,11 +81,8 @@ def _sampled(w: Workload, n_heads=3, n_rows=48, seed=0):
                       + [int(x) for x in rng.integers(0, w.s_q, n_rows)]))
     o_ref, lse_ref = oracle_fwd(w, ins, heads=heads, rows=np.array(rows))
     o_gpu = f64(o.cpu())[:, :, rows]
-    err = max_abs(o_gpu, o_ref)
-    exc = excess_err(o_gpu, o_ref, w.out_dtype)
-    say(f"    max|dO|={err:.3e} beyond-rounding={exc:.3e} relF={rel_fro(o_gpu, o_ref):.3e} heads={heads}")
     tol = TOL["fp8"] if w.dtype == "fp8" else TOL[w.out_dtype]
-    assert exc <= tol, (err, exc)
+    check_out(o_gpu, o_ref, tol, what=f"O heads={heads}: ")
     check_lse(lse.cpu().numpy()[:, :, rows], lse_ref)
     return o, lse, ins, rel_fro(o_gpu, o_ref)
 

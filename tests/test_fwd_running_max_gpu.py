@@ -16,7 +16,7 @@ import torch
 
 import sdpa_inputs
 from sdpa_inputs import Workload
-from tests.parity import TOL, check_lse, excess_err, f64, gpu_fwd, oracle_fwd, rel_fro, say, to_gpu
+from tests.parity import TOL, check_lse, check_out, f64, gpu_fwd, oracle_fwd, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -42,9 +42,7 @@ def _check(w: Workload, ins: dict):
     o, lse = gpu_fwd(w, g)
     o_ref, lse_ref = oracle_fwd(w, ins)
     got = f64(o.cpu())
-    exc = excess_err(got, o_ref, w.out_dtype)
-    say(f"    beyond-rounding={exc:.3e} relF={rel_fro(got, o_ref):.3e}")
-    assert exc <= TOL[w.out_dtype], exc
+    check_out(got, o_ref, TOL[w.out_dtype], what="O: ")
     check_lse(lse.cpu().numpy(), lse_ref)
 
 

@@ -11,9 +11,8 @@ import torch
 import scaled_dot_product_04_amd as sdpa
 import sdpa_inputs
 from oracle import attention_backward, attention_forward
-from oracle import alibi_slopes as oracle_slopes
 from sdpa_inputs import Workload
-from tests.parity import LSE_REL, TOL, excess_err, f64, max_abs, say, to_gpu
+from tests.parity import LSE_REL, TOL, check_out, f64, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -43,10 +42,6 @@ def _check_lse(lg, lr):
     assert err.max() <= LSE_REL, err.max()
 
 
-def test_alibi_slopes_match_oracle():
-    np.testing.assert_allclose(sdpa.alibi_slopes(12, device="cpu").double().numpy(), oracle_slopes(12), rtol=1e-7)
-
-
 @pytest.mark.parametrize("mods", [((2, 4), "f32", False), ((1, 4), "io", True), ((1, 1), "io", False),
                                   (None, None, True), ((2, 1), "f32", True)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
@@ -66,10 +61,7 @@ def test_fwd_score_modifiers(dtype, d, mask, mods):
     causal, align = ALIGN[mask]
     q, k, v = (f64(ins[n]) for n in ("q", "k", "v"))
     o_ref, lse_ref = attention_forward(q, k, v, w.scale, causal, align=align, **_oracle_kw(bias, slopes))
-    og = f64(o.cpu())
-    exc = excess_err(og, o_ref, w.out_dtype)
-    say(f"    O: max|err|={max_abs(og, o_ref):.3e} beyond-rounding={exc:.3e}")
-    assert exc <= TOL[w.out_dtype], exc
+    check_out(f64(o.cpu()), o_ref, TOL[w.out_dtype], what="O: ")
     _check_lse(lse.cpu().numpy(), lse_ref)
 
 
@@ -84,10 +76,7 @@ def _fwd_bwd(w, g, mask, kw, lq=None, lk=None):
 def _check_grads(w, grads, refs):
     tol = 2 * TOL[w.out_dtype]
     for name, x, r in zip(("dq", "dk", "dv"), grads, refs):
-        xa = f64(x.cpu())
-        exc = excess_err(xa, r, w.out_dtype)
-        say(f"    {name}: max|err|={max_abs(xa, r):.3e} beyond-rounding={exc:.3e} max|ref|={np.abs(r).max():.2f}")
-        assert exc <= tol, (name, exc)
+        check_out(f64(x.cpu()), r, tol, grad_dtype=w.out_dtype, what=f"{name}: ")
 
 
 @pytest.mark.parametrize("mods", [((1, 4), "f32", True), ((2, 4), "io", False), (None, None, True)])
@@ -122,8 +111,7 @@ def test_mods_with_padding_bottom_right_gqa(h_kv):
     q, k, v, do = (f64(ins[n]) for n in ("q", "k", "v", "do"))
     kw = dict(seq_len_q=lq.numpy(), seq_len_kv=lk.numpy(), align="bottom_right", **_oracle_kw(bias, slopes))
     o_ref, lse_ref = attention_forward(q, k, v, w.scale, True, **kw)
-    og = f64(o.cpu())
-    assert excess_err(og, o_ref, "bf16") <= TOL["bf16"]
+    check_out(f64(o.cpu()), o_ref, TOL["bf16"], what="O: ")
     _check_lse(lse.cpu().numpy(), lse_ref)
     _check_grads(w, grads, attention_backward(q, k, v, do, w.scale, True, **kw))
 
