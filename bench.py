@@ -273,6 +273,8 @@ def mfma_measured(sdpa, torch, hip, stream, sh) -> dict:
                 cycles, real = s[:, 1] - s[:, 0], s[:, 3] - s[:, 2]
                 clk = float(statistics.median((cycles / real * 0.1).tolist()))  # GHz (real time counts at 100 MHz)
                 best = (ms, clk)
+                log(f"[bench] probe {name}: {ms:.3f} ms, median cycles {statistics.median(cycles.tolist()):.0f}, "
+                    f"median real ticks {statistics.median(real.tolist()):.0f}")
         tf = blocks * 4 * iters * 8 * flops_per / (best[0] / 1e3) / 1e12
         out[f"{name}_tflops"] = round(tf, 1)
         out[f"{name}_clock_ghz"] = round(best[1], 3)

@@ -30,8 +30,10 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint64_t* st
     i32x8 a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      a[i] = 0x38383838 + lane + i;  // e4m3 codes near 1.0
-      b[i] = 0x30303030 + 3 * lane + i;
+      // Finite e4m3 codes only (0x7f / 0xff are NaN): the low byte stays in
+      // 0x38..0x7e for a and 0x30..0x6f for b.
+      a[i] = 0x38383838 + lane + i;
+      b[i] = 0x30303030 + ((3 * lane + i) & 0x3f);
     }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -55,14 +57,15 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint64_t* st
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kChains; ++c) s += acc[c][c];
-  // The sum keeps every chain live; it is stored only when it is NaN (never,
-  // for these operands), so the probe writes nothing but its time stamps.
+  // The sum keeps every chain live. It is stored only when it is NaN (never,
+  // for these finite operands), by the stamping thread itself after its
+  // stamps, where it makes the clock reading obviously wrong.
   if (threadIdx.x == 0) {
     u32x4* out = (u32x4*)(stamps + 4 * blockIdx.x);
     out[0] = u32x4{(uint32_t)t0, (uint32_t)(t0 >> 32), (uint32_t)t1, (uint32_t)(t1 >> 32)};
     out[1] = u32x4{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)};
+    if (s != s) stamps[4 * blockIdx.x] = 0;
   }
-  if (s != s) stamps[4 * blockIdx.x + (lane & 3)] = __builtin_bit_cast(uint32_t, s);
 }
 
 }  // namespace
