@@ -210,6 +210,30 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sdpa_fwd_ex without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, support matrix and results as
+ * sdpa_fwd_ex minus the workspace pair; it calls no hipMalloc / hipFree and
+ * no allocating routine. Where sdpa_fwd_ex would take the split-KV path with a
+ * workspace (see sdpa_fwd_workspace_size), this entry point takes it with a
+ * static scratch array of 64 MiB that the library holds on each GPU it runs
+ * on until the process ends; a shape whose split-KV partials need more than
+ * that returns SDPA_ERR_NOT_SUPPORTED before anything is launched. The scratch
+ * is shared by every call on a GPU and keeps the last call's contents (each
+ * call overwrites every partial it reads), so calls on one GPU that overlap
+ * in time (concurrent streams, or host threads) race: serialise them.
+ */
+sdpa_status_t sdpa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int b, int h_q, int h_kv, int s_q, int s_kv, int d,
+                               const int64_t q_stride[4], const int64_t k_stride[4],
+                               const int64_t v_stride[4], const int64_t o_stride[4],
+                               float attn_scale, sdpa_mask_t mask,
+                               const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                               const sdpa_score_mod_t* mod,
+                               sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype,
+                               const sdpa_fp8_scales_t* fp8, hipStream_t stream);
+
+/*
  * Bytes of device workspace that sdpa_fwd_ex's split-KV path needs for this
  * shape; 0 when the shape does not take it, or takes it without a workspace.
  *

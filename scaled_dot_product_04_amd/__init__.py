@@ -81,6 +81,9 @@ def load_library() -> ctypes.CDLL:
     lib.sdpa_fwd_ex.restype = ctypes.c_int
     lib.sdpa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp,
                                 ctypes.POINTER(ScoreMod), i, i, ctypes.POINTER(Fp8Scales), vp, ctypes.c_size_t, vp]
+    lib.sdpa_fwd_noalloc.restype = ctypes.c_int
+    lib.sdpa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p, f, i, vp, vp,
+                                     ctypes.POINTER(ScoreMod), i, i, ctypes.POINTER(Fp8Scales), vp]
     lib.sdpa_fwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t

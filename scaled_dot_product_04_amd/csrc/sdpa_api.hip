@@ -13,6 +13,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "sdpa.h"
@@ -149,6 +150,47 @@ sdpa_status_t hip_status(hipError_t e, const char* what) {
   return SDPA_OK;
 }
 
+// Scratch of sdpa_fwd_noalloc: the split-KV forward's per-split partials,
+// in a file-scope device array so that the entry point allocates nothing.
+// Each GPU the library runs on holds its own copy until the process ends. In
+// host code `scratch` is only a stand-in for the symbol, not a device address:
+// every use goes through scratch_on(), which resolves the address per device
+// with hipGetSymbolAddress (with that device current) and keeps it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or null with the
+// error recorded.
+void* scratch_on(sdpa_status_t* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(SDPA_ERR_NOT_SUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kMaxDevices - 1);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *st = e != hipSuccess ? hip_status(e, "hipGetSymbolAddress(scratch)")
+                            : fail(SDPA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = SDPA_OK;
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,14 +261,19 @@ size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
   return sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io).ws_bytes;
 }
 
-sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
-                          int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
-                          const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
-                          float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
-                          const int32_t* seq_len_kv, const sdpa_score_mod_t* mod, sdpa_dtype_t in_dtype,
-                          sdpa_dtype_t out_dtype, const sdpa_fp8_scales_t* fp8, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// The forward behind sdpa_fwd_ex and sdpa_fwd_noalloc. With static_scratch the
+// split-KV path takes its partials from the device's static scratch array
+// (the workspace arguments are unused); otherwise from the caller's workspace.
+sdpa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q, int h_kv,
+                       int s_q, int s_kv, int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                       const int64_t v_stride[4], const int64_t o_stride[4], float attn_scale, sdpa_mask_t mask,
+                       const int32_t* seq_len_q, const int32_t* seq_len_kv, const sdpa_score_mod_t* mod,
+                       sdpa_dtype_t in_dtype, sdpa_dtype_t out_dtype, const sdpa_fp8_scales_t* fp8,
+                       void* workspace, size_t workspace_bytes, bool static_scratch, hipStream_t stream) {
   sdpa_status_t st;
   if ((st = check_sizes(b, h_q, h_kv, s_q, s_kv, d)) != SDPA_OK) return st;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
@@ -301,6 +348,14 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   // Few query rows against many keys: the split-KV path, when its workspace
   // (if it needs one) is given; otherwise the row-block kernel.
   const sdpa::DecodePlan plan = sdpa::plan_decode(b, h_q, h_kv, s_q, s_kv, d, io);
+  if (static_scratch && plan.use && !sdpa::has_mod(a.mod) && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(SDPA_ERR_NOT_SUPPORTED,
+                  "the split-KV forward needs %zu bytes of scratch; the static scratch of sdpa_fwd_noalloc holds %zu",
+                  plan.ws_bytes, kScratchBytes);
+    if ((workspace = scratch_on(&st)) == nullptr) return st;
+    workspace_bytes = kScratchBytes;
+  }
   const bool split_kv = plan.use && !sdpa::has_mod(a.mod) && (plan.ws_bytes == 0 || workspace != nullptr);
   if (split_kv && plan.ws_bytes > 0) {
     if (workspace_bytes < plan.ws_bytes)
@@ -324,6 +379,34 @@ sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   }
   if (e == hipSuccess && g_timing.n >= 2) e = hipEventRecord(g_timing.ev[1], stream);
   return hip_status(e, "forward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
+                          int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                          const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
+                          float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
+                          const int32_t* seq_len_kv, const sdpa_score_mod_t* mod, sdpa_dtype_t in_dtype,
+                          sdpa_dtype_t out_dtype, const sdpa_fp8_scales_t* fp8, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  return fwd_impl(q, k, v, o, lse, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride, attn_scale,
+                  mask, seq_len_q, seq_len_kv, mod, in_dtype, out_dtype, fp8, workspace, workspace_bytes, false,
+                  stream);
+}
+
+sdpa_status_t sdpa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h_q,
+                               int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                               const int64_t k_stride[4], const int64_t v_stride[4], const int64_t o_stride[4],
+                               float attn_scale, sdpa_mask_t mask, const int32_t* seq_len_q,
+                               const int32_t* seq_len_kv, const sdpa_score_mod_t* mod, sdpa_dtype_t in_dtype,
+                               sdpa_dtype_t out_dtype, const sdpa_fp8_scales_t* fp8, hipStream_t stream) {
+  g_last_error.clear();
+  return fwd_impl(q, k, v, o, lse, b, h_q, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride, attn_scale,
+                  mask, seq_len_q, seq_len_kv, mod, in_dtype, out_dtype, fp8, nullptr, 0, true, stream);
 }
 
 size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d, int causal,
