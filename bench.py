@@ -310,8 +310,11 @@ def fp8_hd128_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup
                                bf16_ms_step: float) -> dict:
     """Extra measurement (not part of `value`): the hd128 causal training step
     (b2 h16 s8192 d128) with e4m3 tensors and an e5m2 gradient (HYBRID):
-    fp8 forward, then the fp8 backward (widening + 16-bit kernels); TFLOP/s
-    of the same counted flops as the bf16 step, and the speed-up over it."""
+    fp8 forward, then the fp8 backward (all five products on fp8 MFMAs, dS in
+    e4m3); TFLOP/s of the same counted flops as the bf16 step, and the
+    speed-up over it. scale_ds is set the delayed-scaling way before timing:
+    one backward with scale 1 reports max |dS|, the timed ones use the power
+    of two that maps it inside e4m3."""
     w = sdpa_inputs.fp8_hd128()
     ins = sdpa_inputs.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -323,17 +326,25 @@ def fp8_hd128_forward_backward(sdpa, sdpa_inputs, torch, hip, stream, sh, warmup
     dk, dv = sdpa._like_q(g["k"], torch.bfloat16), sdpa._like_q(g["v"], torch.bfloat16)
     ws = torch.empty(max(16, sdpa.bwd_workspace_size(w.b, w.h_q, w.h_kv, w.s_q, w.s_kv, w.d, True,
                                                      torch.float8_e4m3fn)), dtype=torch.uint8, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
     bw = dict(scale=w.scale, causal=True, descale_q=ins["descale_q"], descale_k=ins["descale_k"],
               descale_v=ins["descale_v"], descale_do=ins["descale_do"], dq=dq, dk=dk, dv=dv, workspace=ws,
-              stream=stream)
+              stream=stream, scale_ds=1.0, amax_ds=amax)
 
     def fwd():
         sdpa.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=True, out=o, lse=lse, fp8=sc, stream=stream)
 
+    fwd()
+    sdpa.bwd_fp8(g["q"], g["k"], g["v"], o, g["do"], lse, **bw)
+    torch.cuda.synchronize()
+    bw["scale_ds"] = 2.0 ** math.floor(math.log2(448.0 / max(amax.item(), 1e-30)))
+    bw["amax_ds"] = None
+
     def bwd():
         sdpa.bwd_fp8(g["q"], g["k"], g["v"], o, g["do"], lse, **bw)
 
-    res = {"workload": w.name, "b": w.b, "h": w.h_q, "s": w.s_q, "d": w.d, "formats": "e4m3 q/k/v, e5m2 dO"}
+    res = {"workload": w.name, "b": w.b, "h": w.h_q, "s": w.s_q, "d": w.d,
+           "formats": "e4m3 q/k/v/P/dS, e5m2 dO", "scale_ds": bw["scale_ds"]}
     for name, fn in (("forward", fwd), ("backward", bwd), ("step", lambda: (fwd(), bwd()))):
         for _ in range(warmup):
             fn()

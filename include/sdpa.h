@@ -256,9 +256,10 @@ size_t sdpa_fwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
  * Bytes of device workspace sdpa_bwd needs for this problem (16-byte aligned
  * use): the workspace query of "Using cuDNN in Python" (get_workspace_size(),
  * then a caller-allocated buffer handed to execute). Pure host arithmetic; no
- * error state (invalid shapes give 0). 0 is a valid answer only for empty problems. With dtype
- * SDPA_FP8_E4M3 it is the size sdpa_bwd_fp8 needs (larger: it adds the bf16
- * copies of q, k, v and dout).
+ * error state (invalid shapes give 0). 0 is a valid answer only for empty
+ * problems. The same size serves sdpa_bwd_fp8 (dtype SDPA_FP8_E4M3): both hold
+ * the fp32 row statistic D and, for grouped-query shapes split over several
+ * workgroups, the fp32 dK / dV partials.
  */
 size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int d,
                                int causal, sdpa_dtype_t dtype);
@@ -321,21 +322,39 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
                           sdpa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Per-tensor descale factors of the fp8 backward's inputs: real value =
- * fp8 code * descale (all finite and > 0). */
+/* Factors of the fp8 backward (JAX attention codelab, step 10: per-tensor
+ * scaling, HYBRID format). Inputs: real value = fp8 code * descale (all
+ * finite and > 0). The two products whose left operand the kernels quantise
+ * themselves take a scale: P (softmax weights, <= 1) goes to e4m3 as
+ * P * scale_p, with 0 < scale_p <= 448 (448 uses the whole range); dS (the
+ * score gradient) goes to ds_dtype as dS * scale_ds, saturated to the
+ * format's largest finite value (448 for e4m3, 57344 for e5m2). The recipe's
+ * delayed scaling derives such scales from a history of per-tensor absolute
+ * maxima; amax_ds, when not NULL, is a device float that receives
+ * max(*amax_ds, max |dS|) over this call (dS before scaling and saturation),
+ * which the caller feeds into that history (it must hold a value >= 0, e.g. 0,
+ * before the call). */
 typedef struct {
   float descale_q;
   float descale_k;
   float descale_v;
   float descale_do;
+  float scale_p;           /* e4m3 scale of P; (0, 448] */
+  float scale_ds;          /* scale of dS; finite, > 0 */
+  sdpa_dtype_t ds_dtype;   /* SDPA_FP8_E4M3 or SDPA_FP8_E5M2 */
+  float* amax_ds;          /* optional device float (4-byte aligned), or NULL */
 } sdpa_fp8_bwd_scales_t;
 
 /*
  * FP8 backward: dQ, dK, dV of L = sum(O * dO) for the fp8 forward, in the
  * HYBRID format of the JAX attention codelab (step 10): tensors in e4m3 for
  * the forward pass, the gradient dO in e5m2 for the backward pass, each with a
- * per-tensor scale (the recipe's delayed scaling tracks those factors; they
- * arrive here as descale = 1 / scale).
+ * per-tensor scale. The gradients are those of sdpa_bwd (the exact
+ * chain-rule backward from the forward's LSE), with all five matrix products
+ * on fp8 operands and fp32 accumulation: S = Q K^T and dP = dO V^T on the
+ * codes; dV = P^T dO with P in e4m3 (scale_p); dK = dS^T Q and dQ = dS K with
+ * dS in ds_dtype (scale_ds). The factors of each product are applied to its
+ * fp32 result.
  *
  *   q, k, v     e4m3 codes, [b, h, s, d] with strides as in sdpa_fwd (the
  *               forward's inputs); values q * descale_q etc.
@@ -344,13 +363,11 @@ typedef struct {
  *               value dout * descale_do.
  *   dq, dk, dv  BF16 gradients with respect to the real-valued q, k, v.
  *   mask, seq_len_q, seq_len_kv  as in sdpa_bwd_ex (those of the forward).
+ *   scales      the factors above (required).
  *   workspace   at least sdpa_bwd_workspace_size(..., SDPA_FP8_E4M3) bytes,
  *               16-byte aligned; scratch.
- * Supported: d in {64, 128}; no score modifiers. The codes are widened
- * exactly to bf16 in the workspace (both formats embed in bf16) and the 16-bit
- * backward kernels run on them with the descale factors folded into the
- * softmax scale and the output scales, so the result is that of the BF16
- * backward on the dequantised tensors, up to rounding order.
+ * Supported: d in {64, 128}; no score modifiers. Errors as for sdpa_bwd;
+ * SDPA_ERR_INVALID_ARGUMENT for factors out of range.
  */
 sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse,

@@ -38,9 +38,13 @@ class Fp8Scales(ctypes.Structure):
 
 
 class Fp8BwdScales(ctypes.Structure):
-    """sdpa_fp8_bwd_scales_t: descale factors of the fp8 backward's q, k, v and dO."""
+    """sdpa_fp8_bwd_scales_t: descale factors of the fp8 backward's q, k, v and
+    dO, the quantisation scales of P (e4m3) and dS (ds_dtype), and the optional
+    device pointer that receives max |dS|."""
     _fields_ = [("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
-                ("descale_v", ctypes.c_float), ("descale_do", ctypes.c_float)]
+                ("descale_v", ctypes.c_float), ("descale_do", ctypes.c_float),
+                ("scale_p", ctypes.c_float), ("scale_ds", ctypes.c_float), ("ds_dtype", ctypes.c_int),
+                ("amax_ds", ctypes.c_void_p)]
 
 
 class ScoreMod(ctypes.Structure):
@@ -301,11 +305,17 @@ def bwd(q, k, v, o, dout, lse, *, scale: float, causal=False, dq=None, dk=None, 
 
 
 def bwd_fp8(q, k, v, o, dout, lse, *, scale: float, descale_q: float, descale_k: float,
-            descale_v: float, descale_do: float, causal=False, dq=None, dk=None, dv=None,
+            descale_v: float, descale_do: float, scale_ds: float, scale_p: float = 448.0,
+            ds_dtype=torch.float8_e4m3fn, amax_ds=None, causal=False, dq=None, dk=None, dv=None,
             workspace=None, seq_len_q=None, seq_len_kv=None, stream=None):
     """(dQ, dK, dV) in bf16 for the fp8 forward: q, k, v e4m3, dout e5m2 (or e4m3),
     o the forward's bf16 output, lse its LSE; real values are code * descale.
 
+    scale_p: P is quantised to e4m3 as P * scale_p (0 < scale_p <= 448).
+    scale_ds, ds_dtype: dS is quantised to ds_dtype (float8_e4m3fn or
+    float8_e5m2) as dS * scale_ds, saturating.
+    amax_ds: optional device float32 tensor of one element; receives
+    max(amax_ds, max |dS|) (the caller's scale history input).
     causal, seq_len_q, seq_len_kv: those of the forward that produced o and lse.
     """
     lib = load_library()
@@ -321,7 +331,12 @@ def bwd_fp8(q, k, v, o, dout, lse, *, scale: float, descale_q: float, descale_k:
     if workspace is None:
         n = bwd_workspace_size(b, h_q, h_kv, s_q, s_kv, d, mask != SDPA_MASK_NONE, torch.float8_e4m3fn)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
-    sc = Fp8BwdScales(float(descale_q), float(descale_k), float(descale_v), float(descale_do))
+    if ds_dtype not in (torch.float8_e5m2, torch.float8_e4m3fn):
+        raise TypeError(f"ds_dtype must be float8_e5m2 or float8_e4m3fn, got {ds_dtype}")
+    if amax_ds is not None and (amax_ds.dtype != torch.float32 or amax_ds.numel() < 1 or not amax_ds.is_cuda):
+        raise TypeError("amax_ds must be a float32 device tensor with at least one element")
+    sc = Fp8BwdScales(float(descale_q), float(descale_k), float(descale_v), float(descale_do), float(scale_p),
+                      float(scale_ds), _DTYPE_CODES[ds_dtype], amax_ds.data_ptr() if amax_ds is not None else None)
     _check(lib.sdpa_bwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                             _ptr(dv), b, h_q, h_kv, s_q, s_kv, d, _strides(q), _strides(k), _strides(v),
                             _strides(o), _strides(dout), _strides(dq), _strides(dk), _strides(dv),

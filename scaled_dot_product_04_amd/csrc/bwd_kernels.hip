@@ -678,22 +678,11 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
   }
 }
 
-// Number of workgroups a KV head's query-head group is split over: enough
-// to put at least 512 dK/dV workgroups in flight when the group allows it.
-int choose_split(int b, int h_q, int h_kv, int s_kv) {
-  const int G = h_q / h_kv;
-  const int64_t base = (int64_t)((s_kv + kKvBlock - 1) / kKvBlock) * b * h_kv;
-  int n = 1;
-  while (base * n < 512 && 2 * n <= G && G % (2 * n) == 0) n *= 2;
-  return n;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T, int D, int MOD>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& te) {
   const bool timed = te.n >= 3;
-  const int64_t rows = (int64_t)a.b * a.h_q * a.s_q;
   // dQ first: it also writes D = rowsum(dO * O), which dK/dV reads.
   if (timed) (void)hipEventRecord(te.ev[0], stream);
   const int n_qblk = (a.s_q + 32 * dq_waves(D) - 1) / (32 * dq_waves(D));
@@ -704,8 +693,8 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, MOD>), g2, dim3(64 * dq_waves(D)), 0, stream, a, n_qblk);
   if (timed) (void)hipEventRecord(te.ev[1], stream);
 
-  const int n_split = choose_split(a.b, a.h_q, a.h_kv, a.s_kv);
-  float* part = n_split > 1 ? (float*)((char*)a.delta + align256((size_t)rows * sizeof(float))) : nullptr;
+  const int n_split = bwd_split_count(a.b, a.h_q, a.h_kv, a.s_kv, kKvBlock);
+  float* part = n_split > 1 ? bwd_partials(a) : nullptr;
   const int n_kblk = (a.s_kv + kKvBlock - 1) / kKvBlock;
   const dim3 g1(n_kblk * a.b * a.h_kv * n_split);
   if (a.causal)
@@ -724,9 +713,34 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
 
 }  // namespace
 
+// Number of workgroups a KV head's query-head group is split over: enough
+// to put at least 512 dK/dV workgroups in flight when the group allows it.
+// The workspace is sized for the 256-key blocks of the 16-bit kernels; fewer
+// keys per workgroup give more workgroups, hence never a larger split.
+int bwd_split_count(int b, int h_q, int h_kv, int s_kv, int keys_per_wg) {
+  const int G = h_q / h_kv;
+  const int64_t base = (int64_t)((s_kv + keys_per_wg - 1) / keys_per_wg) * b * h_kv;
+  int n = 1;
+  while (base * n < 512 && 2 * n <= G && G % (2 * n) == 0) n *= 2;
+  return n;
+}
+
+float* bwd_partials(const BwdArgs& a) {
+  const int64_t rows = (int64_t)a.b * a.h_q * a.s_q;
+  return (float*)((char*)a.delta + align256((size_t)rows * sizeof(float)));
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, int n_split, const float* part, hipStream_t stream) {
+  const int64_t n4 = (int64_t)a.b * a.h_kv * a.s_kv * a.d / 4 * 2;
+  const int64_t blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL((bwd_reduce_kernel<Bf16T>), dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
+                     stream, a, n_split, part);
+  return hipGetLastError();
+}
+
 size_t bwd_workspace_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
   size_t bytes = align256((size_t)b * h_q * s_q * sizeof(float));
-  const int n_split = choose_split(b, h_q, h_kv, s_kv);
+  const int n_split = bwd_split_count(b, h_q, h_kv, s_kv, kKvBlock);
   if (n_split > 1) bytes += 2 * (size_t)n_split * b * h_kv * s_kv * d * sizeof(float);
   return bytes;
 }

@@ -1,5 +1,5 @@
 // FP8 (e4m3) forward: fused attention with fp8 inputs, fp32 accumulation and
-// bf16 output; and the widening pass in front of the fp8 backward.
+// bf16 output.
 //
 // What is computed: the same attention as the 16-bit forward (JAX attention
 // codelab, step 1 formula; cuDNN 9 blog, "SDPA as a cuDNN graph", Figure 4),
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
     // m = 16 nb + r of this lane half.
     const float off = lsp - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
     uint32_t pw[8];
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls0, ls1;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int nb = w >> 2, r = 4 * (w & 3);
@@ -250,9 +250,12 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 1], sl2, off));
       const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 2], sl2, off));
       const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r + 3], sl2, off));
-      ls0 += p0 + p2;
-      ls1 += p1 + p3;
-      uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      ls0 = w == 0 ? p0 + p2 : ls0 + (p0 + p2);
+      ls1 = w == 0 ? p1 + p3 : ls1 + (p1 + p3);
+      // The low-half convert keeps the old upper 16 bits, which the high-half
+      // convert then overwrites: any register serves as the old value (p0's
+      // bits here), so no zero has to be materialised first.
+      uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (int)__builtin_bit_cast(uint32_t, p0), false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pw[w] = word;
     }
@@ -305,72 +308,6 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
   return a.d == 128 ? launch_d<128>(a, stream) : launch_d<256>(a, stream);
-}
-
-// ---------------------------------------------------------------------------
-// FP8 backward inputs: exact widening to bf16
-// ---------------------------------------------------------------------------
-// The HYBRID recipe of the JAX attention codelab (step 10) keeps Q, K, V in
-// e4m3 and the gradient dO in e5m2. Every e4m3 value (3 mantissa bits,
-// magnitudes 2^-9 .. 448) and every e5m2 value (2 mantissa bits, 2^-16 ..
-// 57344, inf, NaN) is a bf16 value, so widening the codes loses nothing: the
-// 16-bit backward then runs on the codes themselves, with the per-tensor
-// descale factors folded into its softmax and output scales.
-// One thread widens 16 codes (one 16-byte load, two 16-byte stores); the
-// hardware conversion yields the exact fp32 value and its upper half is the
-// bf16 encoding.
-namespace {
-
-template <bool E5M2, bool HI>
-__device__ __forceinline__ uint32_t widen_pair(uint32_t w) {
-  const f32x2 f = E5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
-}
-
-template <bool E5M2>
-__global__ __launch_bounds__(256) void fp8_widen_kernel(const uint8_t* src, Strides3 st, int h, int s, int d,
-                                                        int64_t rows, uint16_t* dst) {
-  const int cpr = d / 16;  // 16-code chunks per row
-  const int64_t total = rows * cpr;
-  for (int64_t c = blockIdx.x * 256LL + threadIdx.x; c < total; c += (int64_t)gridDim.x * 256) {
-    const int64_t row = c / cpr;
-    const int part = (int)(c % cpr);
-    const int si = (int)(row % s);
-    const int64_t bh = row / s;
-    const int hi = (int)(bh % h);
-    const int64_t bi = bh / h;
-    const u32x4 w = *(const u32x4*)(src + bi * st.b + hi * st.h + (int64_t)si * st.s + part * 16);
-    u32x4 lo, up;
-    lo.x = widen_pair<E5M2, false>(w.x);
-    lo.y = widen_pair<E5M2, true>(w.x);
-    lo.z = widen_pair<E5M2, false>(w.y);
-    lo.w = widen_pair<E5M2, true>(w.y);
-    up.x = widen_pair<E5M2, false>(w.z);
-    up.y = widen_pair<E5M2, true>(w.z);
-    up.z = widen_pair<E5M2, false>(w.w);
-    up.w = widen_pair<E5M2, true>(w.w);
-    uint16_t* o = dst + row * d + part * 16;
-    *(u32x4*)o = lo;
-    *(u32x4*)(o + 8) = up;
-  }
-}
-
-}  // namespace
-
-hipError_t launch_fp8_widen(const void* src, const Strides3& st, int b, int h, int s, int d, bool e5m2, void* dst,
-                            hipStream_t stream) {
-  const int64_t rows = (int64_t)b * h * s;
-  const int64_t chunks = rows * (d / 16);
-  if (chunks == 0) return hipSuccess;
-  const int64_t blocks = (chunks + 255) / 256;
-  const dim3 grid((unsigned)(blocks < 16384 ? blocks : 16384));
-  if (e5m2)
-    hipLaunchKernelGGL((fp8_widen_kernel<true>), grid, dim3(256), 0, stream, (const uint8_t*)src, st, h, s, d, rows,
-                       (uint16_t*)dst);
-  else
-    hipLaunchKernelGGL((fp8_widen_kernel<false>), grid, dim3(256), 0, stream, (const uint8_t*)src, st, h, s, d, rows,
-                       (uint16_t*)dst);
-  return hipGetLastError();
 }
 
 }  // namespace sdpa

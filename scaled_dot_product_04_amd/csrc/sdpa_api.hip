@@ -58,12 +58,6 @@ bool valid_dtype(int t) { return t >= SDPA_F32 && t <= SDPA_FP8_E5M2; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Bytes of the fp8 backward's bf16 copies of q, dout (b*h_q*s_q*d each) and
-// k, v (b*h_kv*s_kv*d each), placed after the 16-bit backward's workspace.
-size_t fp8_stage_bytes(int b, int h_q, int h_kv, int s_q, int s_kv, int d) {
-  return 2 * align256((size_t)b * h_q * s_q * d * 2) + 2 * align256((size_t)b * h_kv * s_kv * d * 2);
-}
-
 // Checks one tensor's pointer and strides. Returns SDPA_OK or an error.
 sdpa_status_t check_tensor(const char* name, const void* p, const int64_t* st, int eb,
                            sdpa::Strides3* out) {
@@ -413,9 +407,8 @@ size_t sdpa_bwd_workspace_size(int b, int h_q, int h_kv, int s_q, int s_kv, int 
                                sdpa_dtype_t dtype) {
   (void)causal;
   if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_kv <= 0 || d <= 0) return 0;
-  const size_t base = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
-  if (dtype == SDPA_FP8_E4M3) return align256(base) + fp8_stage_bytes(b, h_q, h_kv, s_q, s_kv, d);
-  return base;
+  (void)dtype;  // the fp8 backward needs the same D and partial buffers
+  return sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
 }
 
 sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -515,15 +508,13 @@ sdpa_status_t sdpa_bwd_ex(const void* q, const void* k, const void* v, const voi
 }
 
 // The fp8 backward (JAX attention codelab, step 10, HYBRID format). With
-// codes Qc, Kc, Vc, dOc and descales sq, sk, sv, so (real X = Xc * sX):
-//   S     = attn_scale * sq * sk * Qc Kc^T          (softmax scale)
-//   dP    = so * sv * dOc Vc^T,  D = so * rowsum(dOc * O)
-//   dS    = P * (dP - D) = so * sv * P * (dOc Vc^T - D / (so * sv))
-// so the 16-bit kernels run on the widened codes with
-//   delta_scale = 1 / sv, dS' = P * (dOc Vc^T - rowsum(dOc * O) / sv),
-//   dQ = attn_scale * dS K   = (attn_scale * so * sv * sk) * dS' Kc,
-//   dK = attn_scale * dS^T Q = (attn_scale * so * sv * sq) * dS'^T Qc,
-//   dV = P^T dO              = so * P^T dOc.
+// codes Qc, Kc, Vc, dOc and descales sq, sk, sv, so (real X = Xc * sX), and
+// the kernels' quantised Pc = e4m3(P * sp), dSc = fp8(dS * sds):
+//   S  = attn_scale * sq * sk * Qc Kc^T      (softmax scale)
+//   dP = so * sv * dOc Vc^T,  D = so * rowsum(dOc * O),  dS = P * (dP - D)
+//   dQ = attn_scale * dS K   = (attn_scale * sk / sds) * dSc Kc
+//   dK = attn_scale * dS^T Q = (attn_scale * sq / sds) * dSc^T Qc
+//   dV = P^T dO              = (so / sp) * Pc^T dOc
 sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, int b, int h_q, int h_kv, int s_q,
                            int s_kv, int d, const int64_t q_stride[4], const int64_t k_stride[4],
@@ -540,10 +531,17 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
     return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_scale must be finite and > 0");
   if (do_dtype != SDPA_FP8_E5M2 && do_dtype != SDPA_FP8_E4M3)
     return fail(SDPA_ERR_INVALID_ARGUMENT, "do_dtype must be FP8_E5M2 or FP8_E4M3 (got %d)", (int)do_dtype);
-  if (scales == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 descale factors are NULL");
+  if (scales == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 scale factors are NULL");
   const float sq = scales->descale_q, sk = scales->descale_k, sv = scales->descale_v, so = scales->descale_do;
   for (float x : {sq, sk, sv, so})
     if (!(x > 0.f) || !isfinite(x)) return fail(SDPA_ERR_INVALID_ARGUMENT, "fp8 descale factors must be finite and > 0");
+  const float sp = scales->scale_p, sds = scales->scale_ds;
+  if (!(sp > 0.f) || !(sp <= 448.f))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "scale_p must be in (0, 448] (P * scale_p must fit e4m3), got %g", sp);
+  if (!(sds > 0.f) || !isfinite(sds)) return fail(SDPA_ERR_INVALID_ARGUMENT, "scale_ds must be finite and > 0");
+  if (scales->ds_dtype != SDPA_FP8_E4M3 && scales->ds_dtype != SDPA_FP8_E5M2)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "ds_dtype must be FP8_E4M3 or FP8_E5M2 (got %d)", (int)scales->ds_dtype);
+  if (((uintptr_t)scales->amax_ds) % 4 != 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "amax_ds is not 4-byte aligned");
   if (!(d == 64 || d == 128)) return fail(SDPA_ERR_NOT_SUPPORTED, "no fp8 backward for d=%d", d);
   sdpa::BwdArgs a{};
   a.mod.drop_k8 = 256;  // no score modifiers
@@ -562,50 +560,29 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
     return hip_status(sdpa::launch_zero_dkdv(a, sdpa::Io::BF16, stream), "zero dK/dV launch");
   }
   if (lse == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse is required by the backward");
-  sdpa::Strides3 qs8, ks8, vs8, dos8;
-  if ((st = check_tensor("q", q, q_stride, 1, &qs8)) != SDPA_OK) return st;
-  if ((st = check_tensor("k", k, k_stride, 1, &ks8)) != SDPA_OK) return st;
-  if ((st = check_tensor("v", v, v_stride, 1, &vs8)) != SDPA_OK) return st;
-  if ((st = check_tensor("dout", dout, do_stride, 1, &dos8)) != SDPA_OK) return st;
+  if ((st = check_tensor("q", q, q_stride, 1, &a.qs)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, 1, &a.ks)) != SDPA_OK) return st;
+  if ((st = check_tensor("v", v, v_stride, 1, &a.vs)) != SDPA_OK) return st;
+  if ((st = check_tensor("dout", dout, do_stride, 1, &a.dos)) != SDPA_OK) return st;
   if ((st = check_tensor("o", o, o_stride, 2, &a.os)) != SDPA_OK) return st;
   if ((st = check_tensor("dq", dq, dq_stride, 2, &a.dqs)) != SDPA_OK) return st;
   if ((st = check_tensor("dk", dk, dk_stride, 2, &a.dks)) != SDPA_OK) return st;
   if ((st = check_tensor("dv", dv, dv_stride, 2, &a.dvs)) != SDPA_OK) return st;
   if (((uintptr_t)lse) % 4 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "lse is not 4-byte aligned");
-  const size_t base = align256(sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d));
-  const size_t need = base + fp8_stage_bytes(b, h_q, h_kv, s_q, s_kv, d);
+  const size_t need = sdpa::bwd_workspace_bytes(b, h_q, h_kv, s_q, s_kv, d);
   if (workspace_bytes < need)
     return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (workspace == nullptr) return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (((uintptr_t)workspace) % 16 != 0) return fail(SDPA_ERR_NOT_SUPPORTED, "workspace is not 16-byte aligned");
-  // Workspace: [16-bit backward's scratch][q16][do16][k16][v16], compact [b][h][s][d] bf16.
-  char* w = (char*)workspace;
-  const size_t qbytes = align256((size_t)b * h_q * s_q * d * 2), kbytes = align256((size_t)b * h_kv * s_kv * d * 2);
-  void* q16 = w + base;
-  void* do16 = w + base + qbytes;
-  void* k16 = w + base + 2 * qbytes;
-  void* v16 = w + base + 2 * qbytes + kbytes;
-  const sdpa::Strides3 cq{(int64_t)h_q * s_q * d, (int64_t)s_q * d, d};
-  const sdpa::Strides3 ck{(int64_t)h_kv * s_kv * d, (int64_t)s_kv * d, d};
-  hipError_t e;
-  if ((e = sdpa::launch_fp8_widen(q, qs8, b, h_q, s_q, d, false, q16, stream)) != hipSuccess ||
-      (e = sdpa::launch_fp8_widen(dout, dos8, b, h_q, s_q, d, do_dtype == SDPA_FP8_E5M2, do16, stream)) != hipSuccess ||
-      (e = sdpa::launch_fp8_widen(k, ks8, b, h_kv, s_kv, d, false, k16, stream)) != hipSuccess ||
-      (e = sdpa::launch_fp8_widen(v, vs8, b, h_kv, s_kv, d, false, v16, stream)) != hipSuccess)
-    return hip_status(e, "fp8 widening launch");
-  a.q = q16;
-  a.k = k16;
-  a.v = v16;
+  a.q = q;
+  a.k = k;
+  a.v = v;
   a.o = o;
-  a.dout = do16;
+  a.dout = dout;
   a.lse = lse;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.qs = cq;
-  a.dos = cq;
-  a.ks = ck;
-  a.vs = ck;
   a.b = b;
   a.h_q = h_q;
   a.h_kv = h_kv;
@@ -616,16 +593,24 @@ sdpa_status_t sdpa_bwd_fp8(const void* q, const void* k, const void* v, const vo
   a.bottom_right = mask == SDPA_MASK_CAUSAL_BOTTOM_RIGHT;
   a.seq_q = seq_len_q;
   a.seq_kv = seq_len_kv;
+  // Real values: Q = q * sq, K = k * sk, V = v * sv, dO = do * so, P = p8 / sp,
+  // dS = ds8 / sds; each product's factors multiply its fp32 accumulator.
   a.scale = attn_scale * sq * sk;
-  a.dq_scale = attn_scale * so * sv * sk;
-  a.dk_scale = attn_scale * so * sv * sq;
-  a.dv_scale = so;
-  a.delta_scale = 1.f / sv;
+  a.dq_scale = attn_scale * sk / sds;
+  a.dk_scale = attn_scale * sq / sds;
+  a.dv_scale = so / sp;
+  a.delta_scale = so;
   a.delta = (float*)workspace;
+  a.f8.dp_scale = so * sv;
+  a.f8.scale_p = sp;
+  a.f8.scale_ds = sds;
+  a.f8.amax_ds = scales->amax_ds;
+  a.f8.do_e5m2 = do_dtype == SDPA_FP8_E5M2;
+  a.f8.ds_e5m2 = scales->ds_dtype == SDPA_FP8_E5M2;
   if (log_level() >= 2)
-    fprintf(stderr, "[sdpa] bwd_fp8 d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d do=%d\n", d, b, h_q, h_kv, s_q,
-            s_kv, (int)mask, (int)do_dtype);
-  return hip_status(sdpa::launch_bwd(a, sdpa::Io::BF16, stream, g_timing), "fp8 backward launch");
+    fprintf(stderr, "[sdpa] bwd_fp8 d=%d b=%d h_q=%d h_kv=%d s_q=%d s_kv=%d mask=%d do=%d ds=%d\n", d, b, h_q, h_kv,
+            s_q, s_kv, (int)mask, (int)do_dtype, (int)scales->ds_dtype);
+  return hip_status(sdpa::launch_bwd_fp8(a, stream, g_timing), "fp8 backward launch");
 }
 
 }  // extern "C"

@@ -83,6 +83,15 @@ struct BwdArgs {
   float dv_scale;     // dV = dv_scale * P^T dO    (1)
   float delta_scale;  // D_i = delta_scale * sum_d dO_id * O_id (1)
   float* delta;  // workspace: fp32 [b][h_q][s_q], D_i = sum_d dO_id * O_id
+  // fp8 backward only (codes in, the 16-bit path ignores these)
+  struct {
+    float dp_scale;   // dP = dp_scale * (dO codes . V codes)
+    float scale_p;    // P is quantised to e4m3 as P * scale_p
+    float scale_ds;   // dS is quantised as dS * scale_ds (saturating)
+    float* amax_ds;   // optional: max-combined with max |dS| (bit pattern, >= 0)
+    int do_e5m2;      // dO codes are e5m2 (else e4m3)
+    int ds_e5m2;      // dS is quantised to e5m2 (else e4m3)
+  } f8;
 };
 
 // Split-KV forward (few query rows, many keys): partial results of each key
@@ -116,11 +125,15 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 DecodePlan plan_decode(int b, int h_q, int h_kv, int s_q, int s_kv, int d, Io io);
 hipError_t launch_fwd_decode(const FwdArgs& a, const DecodePlan& p, void* workspace, Io io, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, Io io, hipStream_t stream, const TimingEvents& te);
+// fp8 backward (codes in a.q, a.k, a.v, a.dout; bf16 o, dq, dk, dv); d 64 or 128.
+hipError_t launch_bwd_fp8(const BwdArgs& a, hipStream_t stream, const TimingEvents& te);
 hipError_t launch_zero_dkdv(const BwdArgs& a, Io io, hipStream_t stream);
-// Exact widening of fp8 codes (e5m2 when e5m2, else e4m3) of a strided
-// [b][h][s][d] tensor into a compact bf16 [b][h][s][d] copy at dst.
-hipError_t launch_fp8_widen(const void* src, const Strides3& st, int b, int h, int s, int d, bool e5m2,
-                            void* dst, hipStream_t stream);
+// Query-head split of the dK/dV kernels (1: none) and, when it is > 1, their
+// fp32 partials in the workspace after D, and the kernel that sums them in
+// split order into bf16 dK, dV.
+int bwd_split_count(int b, int h_q, int h_kv, int s_kv, int keys_per_wg);
+float* bwd_partials(const BwdArgs& a);
+hipError_t launch_bwd_reduce(const BwdArgs& a, int n_split, const float* part, hipStream_t stream);
 
 // Matrix-core rate probe (bf16 32x32x16 or fp8 32x32x64 MFMAs); stamps get
 // 4 uint64 per workgroup: shader cycles and real time at loop start and end.

@@ -202,11 +202,18 @@ def test_dropout_probability_validated():
     assert st == 1 and "dropout_p" in msg
 
 
+def _bscales(**kw):
+    f = dict(descale_q=0.01, descale_k=0.01, descale_v=0.01, descale_do=1e-4, scale_p=448.0, scale_ds=1.0,
+             ds_dtype=sdpa.SDPA_FP8_E4M3, amax_ds=None)
+    f.update(kw)
+    return sdpa.Fp8BwdScales(**f)
+
+
 def _bwd_fp8(**kw):
     lib = sdpa.load_library()
     b, hq, hkv, s, d = 2, 4, 2, 64, 128
     a = dict(q=FAKE, do=FAKE, b=b, d=d, mask=1, do_dtype=sdpa.SDPA_FP8_E5M2,
-             scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.01, 0.01, 1e-4)), ws_bytes=1 << 30, qs8=None)
+             scales=ctypes.pointer(_bscales()), ws_bytes=1 << 30, qs8=None)
     a.update(kw)
     S = ctypes.c_int64 * 4
     q16, k16 = S(*_bshd(b, hq, s, d)), S(*_bshd(b, hkv, s, d))
@@ -223,8 +230,14 @@ def _bwd_fp8(**kw):
     (dict(mask=4), 1, "mask must be"),
     (dict(do_dtype=sdpa.SDPA_BF16), 1, "do_dtype"),
     (dict(scales=None), 1, "NULL"),
-    (dict(scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.0, 0.01, 1e-4))), 1, "finite and > 0"),
-    (dict(scales=ctypes.pointer(sdpa.Fp8BwdScales(0.01, 0.01, float("inf"), 1e-4))), 1, "finite and > 0"),
+    (dict(scales=ctypes.pointer(_bscales(descale_k=0.0))), 1, "finite and > 0"),
+    (dict(scales=ctypes.pointer(_bscales(descale_v=float("inf")))), 1, "finite and > 0"),
+    (dict(scales=ctypes.pointer(_bscales(scale_p=0.0))), 1, "scale_p"),
+    (dict(scales=ctypes.pointer(_bscales(scale_p=449.0))), 1, "scale_p"),
+    (dict(scales=ctypes.pointer(_bscales(scale_ds=0.0))), 1, "scale_ds"),
+    (dict(scales=ctypes.pointer(_bscales(scale_ds=float("nan")))), 1, "scale_ds"),
+    (dict(scales=ctypes.pointer(_bscales(ds_dtype=sdpa.SDPA_BF16))), 1, "ds_dtype"),
+    (dict(scales=ctypes.pointer(_bscales(amax_ds=0x1002))), 1, "amax_ds"),
     (dict(d=256), 2, "no fp8 backward"),
     (dict(ws_bytes=16), 3, "workspace"),
     # an fp8 row of 128 codes with a 136-byte stride is not 16-byte aligned
@@ -236,14 +249,14 @@ def test_backward_fp8_validation_errors(kw, status, needle):
     assert needle in msg
 
 
-def test_fp8_backward_workspace_holds_bf16_copies():
+def test_fp8_backward_workspace_matches_16bit():
+    """The fp8 backward runs on the codes themselves: its workspace is the
+    16-bit backward's (D, plus the split partials of grouped-query shapes)."""
     f = sdpa.load_library().sdpa_bwd_workspace_size
-    b, hq, hkv, s, d = 2, 16, 4, 1024, 128
-    plain = f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_BF16)
-    fp8 = f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_FP8_E4M3)
-    # q and dO (b*h_q*s*d each) and k, v (b*h_kv*s*d each) as bf16
-    assert fp8 >= plain + 2 * 2 * b * s * d * (hq + hkv)
-    assert fp8 % 16 == 0
+    for b, hq, hkv, s, d in ((2, 16, 4, 1024, 128), (1, 32, 1, 512, 64), (2, 16, 16, 8192, 128)):
+        plain = f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_BF16)
+        assert f(b, hq, hkv, s, s, d, 1, sdpa.SDPA_FP8_E4M3) == plain
+        assert plain >= 4 * b * hq * s and plain % 16 == 0
     st, msg = _fwd_ex(tin=sdpa.SDPA_FP8_E5M2)  # e5m2 is a gradient format only
     assert st == 2 and "no forward kernel" in msg
 
