@@ -170,35 +170,42 @@ __device__ __forceinline__ i32x8 lds_op16x2(const uint8_t* p0, const uint8_t* p1
 // dK / dV
 // ---------------------------------------------------------------------------
 // A workgroup owns 128 keys. Waves 0..3 (role dV) and 4..7 (role dK) share
-// them: wave w and wave w + 4 both own keys 32 (w % 4) .. + 31, and run on the
-// same SIMD. The dV wave computes S, P and dV^T += dO^T P (8 MFMAs per 64-row
-// tile); the dK wave S, dP, dS and dK^T += Q^T dS (12). With one set of
-// accumulators each (64 registers), a wave fits in the 256 registers that two
-// waves per SIMD leave it; one wave holding both would need more, and spill.
-// S is formed twice, which costs 4 of 20 MFMAs per tile.
+// them: wave w and wave w + 4 both own keys 32 (w % 4) .. + 31 and run on the
+// same SIMD. Per 64-row tile t:
+//   dV wave: S = Q K^T, P (masked), dV^T += dO^T P; it also leaves P * scale_p
+//            (fp16, lane-private layout) in LDS for its dK partner;
+//   dK wave: one tile behind: dS for tile t - 1 from that P and the dP it
+//            formed at the previous step, dK^T += Q^T dS; then dP = dO V^T
+//            for tile t, held in registers until P(t) arrives.
+// So every product is formed once (16 MFMAs per tile and key slice), each
+// wave holds one accumulator set (64 registers), the exponentials are taken
+// once, and one barrier per tile still orders everything: P(t) is written
+// before the barrier that starts step t + 1, where the dK wave reads it. The
+// Q^T tile and D values stay one step longer (three buffers). Masked scores
+// give P = 0, hence dS = 0: the dK wave needs no mask.
 template <int D, bool CAUSAL, bool DO_E5M2, bool DS_E5M2, bool AMAX>
 __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_split, float* part) {
   typedef Geo8<D> G;
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   constexpr int NKS = D / 64, NDB = D / 32;
   constexpr int FDO = DO_E5M2 ? 1 : 0, FDS = DS_E5M2 ? 1 : 0;
   static_assert(2 * G::BPT <= kNT8 && G::BPT <= kNT8 / 2, "staging map");
+  // P exchange: per key slice, 64 lanes x 32 fp16 (64 bytes) at an 80-byte
+  // pitch (16 lanes storing one 16-byte piece each hit distinct 4-bank groups).
+  constexpr int PXP = 80, PXS = 64 * PXP;
   __shared__ __attribute__((aligned(16))) uint8_t Qr[2][G::ROW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Dr[2][G::ROW_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Qt[2][G::T_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Dt[2][G::T_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Qt[3][G::T_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Px[2][4 * PXS];
   __shared__ __attribute__((aligned(16))) float lse2s[2][kT8];
-  __shared__ __attribute__((aligned(16))) float dels[2][kT8];
-  // The block's K and V rows for the whole kernel: row r holds K row r, V row
-  // r and 16 bytes of padding (pitch 68 dwords: 16 lanes reading one 16-byte
-  // chunk of 16 consecutive rows hit distinct 4-bank groups).
-  constexpr int KVP = 2 * D + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t KV[kKeys8 * KVP];
+  __shared__ __attribute__((aligned(16))) float dels[3][kT8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const bool role_dk = wu >= 4;
-  const int kw = wu & 3;  // key sub-block of this wave
+  const int kw = wu & 3;  // key slice of this wave
   const int n_slots = a.b * a.h_kv * n_split;
   const int kb = blockIdx.x / n_slots;
   const int slot = xcd_slot(blockIdx.x - kb * n_slots, n_slots, n_split);
@@ -210,28 +217,26 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
 
   const int kw0 = kb * kKeys8 + kw * 32;
   const int my_key = kw0 + j;
-  // Stage the block's K and V rows once (keys at or past lk read as zero);
-  // the first barrier of the tile loop orders these stores before any read.
+  // This lane's K row (dV wave: B operand of S) or V row (dK wave: of dP),
+  // bytes 64 t + 32 h .. + 31; keys at or past lk read as zero.
+  i32x8 kvf[NKS];
   {
-    constexpr int CPR = D / 16;  // 16-byte chunks per row
     const int k0 = kb * kKeys8;
-    const uint8_t* kp = (const uint8_t*)a.k + bi * a.ks.b + g * a.ks.h + (int64_t)k0 * a.ks.s;
-    const uint8_t* vp = (const uint8_t*)a.v + bi * a.vs.b + g * a.vs.h + (int64_t)k0 * a.vs.s;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, tile_bytes(k0, L.lk, a.ks.s, D, 1));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, tile_bytes(k0, L.lk, a.vs.s, D, 1));
+    const Strides3 st = role_dk ? a.vs : a.ks;
+    const uint8_t* base = (const uint8_t*)(role_dk ? a.v : a.k) + bi * st.b + g * st.h + (int64_t)k0 * st.s;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, tile_bytes(k0, L.lk, st.s, D, 1));
 #pragma unroll
-    for (int i = 0; i < kKeys8 * CPR / kNT8; ++i) {
-      const int c = tid + kNT8 * i;
-      const int r = c / CPR, cc = c % CPR;
-      *(u32x4*)(&KV[r * KVP + 16 * cc]) = buf_load16(kr, (uint32_t)(r * a.ks.s + 16 * cc));
-      *(u32x4*)(&KV[r * KVP + D + 16 * cc]) = buf_load16(vr, (uint32_t)(r * a.vs.s + 16 * cc));
+    for (int t = 0; t < NKS; ++t) {
+      const uint32_t o = (uint32_t)((kw * 32 + j) * st.s + 64 * t + 32 * h);
+      const u32x4 x0 = buf_load16(rs, o), x1 = buf_load16(rs, o + 16);
+      kvf[t] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
   }
-  // This lane's K / V row (B operands of S and dP): bytes 64 t + 32 h .. + 31.
-  const int kvoff = (kw * 32 + j) * KVP + 32 * h;
   f32x16 acc[NDB];  // dV^T (role dV) or dK^T (role dK)
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  f32x16 dph[2];  // dK wave: dP of the tile whose P is still to come
+  dph[0] = dph[1] = f32x16{};
   // Weights are produced pre-multiplied by scale_p (the log2 of it is folded
   // into the exponent), and dS * scale_ds as p' * (dP' - D') with the
   // factors folded: dP' = dp_acc * dp_scale * scale_ds / scale_p, D' = D *
@@ -242,6 +247,11 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
   const float dlf = a.f8.scale_ds / a.f8.scale_p;
   constexpr float FMAX = fp8_max<DS_E5M2>();
   float amax = 0.f;  // max |dS * scale_ds| of this lane (role dK)
+  // An addend of 0 the compiler cannot see as a constant: with it, p' * t
+  // with p' in fp16 is one v_fma_mix_f32 (a plain product would convert p'
+  // first).
+  float zero;
+  asm("s_mov_b32 %0, 0" : "=s"(zero));
 
   const int n_qt = (L.lq + kT8 - 1) / kT8;
   const int qt0 = CAUSAL ? min(n_qt, max(0, kb * kKeys8 - L.off) / kT8) : 0;
@@ -281,115 +291,150 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
       creg = a.delta[row];
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int b2, int b3) {
     if (st_q) {
-      blk.store_rows(Qr[buf]);
-      blk.store_cols(Qt[buf]);
+      blk.store_rows(Qr[b2]);
+      blk.store_cols(Qt[b3]);
     } else if (st_d) {
-      blk.store_rows(Dr[buf]);
-      blk.store_cols(Dt[buf]);
+      blk.store_rows(Dr[b2]);
+      blk.store_cols(Dt[b2]);
     }
     if (tid < kT8) {
       // A row that sees no key has LSE = -inf and every score masked; 0 keeps
       // exp2(-inf - lse) at 0 instead of NaN.
-      lse2s[buf][tid] = (lvalid && lreg != -INFINITY) ? lreg * kLog2e - lsp : 0.f;
-      dels[buf][tid] = lvalid ? creg * dlf : 0.f;
+      lse2s[b2][tid] = (lvalid && lreg != -INFINITY) ? lreg * kLog2e - lsp : 0.f;
+      dels[b3][tid] = lvalid ? creg * dlf : 0.f;
     }
   };
 
-  // Per-lane LDS offsets: A-operand row j of each 32-row block, and the
-  // transposed rows 32 db + j (two 16-row runs, 16 h and 32 + 16 h).
+  // Per-lane LDS offsets: A-operand row j of each 32-row block, the
+  // transposed rows 32 db + j (two 16-row runs, 16 h and 32 + 16 h), and this
+  // lane's P exchange slot.
   const int rowoff = j * G::RSTR + 32 * h;
   const int troff = G::trow(j) + 16 * h;
+  const int pxoff = kw * PXS + lane * PXP;
+
+  // dK wave: dS and dK for the tile whose dP is in dph, P in Px[pb], Q^T in
+  // Qt[b3], D in dels[b3].
+  auto dk_finish = [&](int pb, int b3) __attribute__((always_inline)) {
+    // Read as eight fp16 values per 16 bytes. (Bit-casting single 32-bit
+    // elements of a 4 x u32 vector to two fp16 values and converting them has
+    // been compiled into reads of element 0 only.)
+    f16x8 pw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pw[c] = __builtin_bit_cast(f16x8, *(const u32x4*)(&Px[pb][pxoff + 16 * c]));
+    uint32_t sk[8];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int row0 = 32 * nb + 16 * h + 4 * w;
+        const f32x4 d4 = *(const f32x4*)(&dels[b3][row0]);
+        float ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // dS * scale_ds
+          ds[e] = fmaf((float)pw[2 * nb + w / 2][4 * (w % 2) + e], fmaf(dph[nb][4 * w + e], dpf, -d4[e]), zero);
+        // The reported maximum is taken before saturation, so that a scale
+        // history sees the values that did not fit.
+        if (AMAX) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(ds[0]), fabsf(ds[1])), fmaxf(fabsf(ds[2]), fabsf(ds[3]))));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[e] = __builtin_amdgcn_fmed3f(ds[e], -FMAX, FMAX);
+        sk[4 * nb + w] = pack4_fp8<DS_E5M2>(ds[0], ds[1], ds[2], ds[3]);
+      }
+    const i32x8 sb = i32x8{(int)sk[0], (int)sk[1], (int)sk[2], (int)sk[3], (int)sk[4], (int)sk[5], (int)sk[6], (int)sk[7]};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int o = troff + db * G::TDB;
+      acc[db] = mfma8<0, FDS>(lds_op16x2(&Qt[b3][o], &Qt[b3][o + 32]), sb, acc[db]);
+    }
+  };
 
   if (n_it > 0) {
     load_tile();
-    store_tile(0);
+    store_tile(0, 0);
     if (n_it > 1) load_tile();
   }
   int cur_qt = qt0 - 1;
+  int b3 = 0;             // buffer of the tile being computed among the three-deep ones
+  bool prev_live = false;  // the previous tile had work for this key slice (dK wave)
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
+    const int b3n = b3 == 2 ? 0 : b3 + 1, b3p = b3 == 0 ? 2 : b3 - 1;
     cur_qt = cur_qt + 1 == qt0 + nq ? qt0 : cur_qt + 1;
     const int q0 = cur_qt * kT8;
-    __syncthreads();  // buffer `buf` is complete; buffer buf ^ 1 is no longer read
+    __syncthreads();  // tile `it` and P of tile it - 1 are in LDS; nothing still reads the buffers written next
     if (it + 1 < n_it) {
-      store_tile(buf ^ 1);
+      store_tile(buf ^ 1, b3n);
       if (it + 2 < n_it) load_tile();
     }
-    // Tiles whose queries all precede this wave's keys add nothing.
-    if (CAUSAL && q0 + kT8 - 1 + L.off < kw0) continue;
-    const bool need_mask = (q0 + kT8 > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
-    // The tile body exists once per role and mask state, each one
-    // branch-free: a mask branch inside a body would split it into blocks
-    // across which the hoisted operand reads stay live.
-    auto body = [&](auto dk_role, auto masked) __attribute__((always_inline)) {
-      constexpr bool DK = decltype(dk_role)::value, MASKED = decltype(masked)::value;
-      uint32_t pk[8];  // P (role dV) or dS (role dK), packed as the B operand
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        // S (and dP) for tile rows 32 nb + 16 h + r (register r) x this lane's key.
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NKS; ++t) {
-          s = mfma8<0, 0>(lds_op32(&Qr[buf][nb * 32 * G::RSTR + rowoff + 64 * t]), lds_op32(&KV[kvoff + 64 * t]), s);
-          if (DK)
-            dp = mfma8<FDO, 0>(lds_op32(&Dr[buf][nb * 32 * G::RSTR + rowoff + 64 * t]),
-                               lds_op32(&KV[kvoff + D + 64 * t]), dp);
-        }
-        if (MASKED) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + 32 * nb + 16 * h + r;
-            if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int row0 = 32 * nb + 16 * h + 4 * w;
-          const f32x4 l4 = *(const f32x4*)(&lse2s[buf][row0]);
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * w + e], sl2, -l4[e]));  // P * scale_p
-          if (DK) {
-            const f32x4 d4 = *(const f32x4*)(&dels[buf][row0]);
-            float ds[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ds[e] = p[e] * fmaf(dp[4 * w + e], dpf, -d4[e]);  // dS * scale_ds
-            // The reported maximum is taken before saturation, so that a
-            // scale history sees the values that did not fit.
-            if (AMAX) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(ds[0]), fabsf(ds[1])), fmaxf(fabsf(ds[2]), fabsf(ds[3]))));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ds[e] = __builtin_amdgcn_fmed3f(ds[e], -FMAX, FMAX);
-            pk[4 * nb + w] = pack4_fp8<DS_E5M2>(ds[0], ds[1], ds[2], ds[3]);
-          } else {
-            pk[4 * nb + w] = pack4_fp8<false>(p[0], p[1], p[2], p[3]);
-          }
-        }
-      }
-      const i32x8 pb = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
-      // dV^T += dO^T P, or dK^T += Q^T dS, over the tile's 64 rows.
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int o = troff + db * G::TDB;
-        if (DK)
-          acc[db] = mfma8<0, FDS>(lds_op16x2(&Qt[buf][o], &Qt[buf][o + 32]), pb, acc[db]);
-        else
-          acc[db] = mfma8<FDO, 0>(lds_op16x2(&Dt[buf][o], &Dt[buf][o + 32]), pb, acc[db]);
-      }
-    };
+    // A tile whose queries all precede this slice's keys has no work.
+    const bool live = !(CAUSAL && q0 + kT8 - 1 + L.off < kw0);
     if (role_dk) {
+      if (prev_live) dk_finish(buf ^ 1, b3p);
+      if (live) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          f32x16 dp = f32x16{};
+#pragma unroll
+          for (int t = 0; t < NKS; ++t)
+            dp = mfma8<FDO, 0>(lds_op32(&Dr[buf][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], dp);
+          dph[nb] = dp;
+        }
+      }
+      prev_live = live;
+    } else if (live) {
+      const bool need_mask = (q0 + kT8 > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
+      // The body exists with and without the mask, each one branch-free: a
+      // mask branch inside it would split it into blocks across which the
+      // hoisted operand reads stay live.
+      auto dv_body = [&](auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
+        uint32_t pk[8];
+        u32x4 ph[4];  // P * scale_p as fp16 pairs, for the dK wave
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          // S for tile rows 32 nb + 16 h + r (register r) x this lane's key.
+          f32x16 s = f32x16{};
+#pragma unroll
+          for (int t = 0; t < NKS; ++t)
+            s = mfma8<0, 0>(lds_op32(&Qr[buf][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], s);
+          if (MASKED) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qi = q0 + 32 * nb + 16 * h + r;
+              if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x4 l4 = *(const f32x4*)(&lse2s[buf][32 * nb + 16 * h + 4 * w]);
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * w + e], sl2, -l4[e]));  // P * scale_p
+            pk[4 * nb + w] = pack4_fp8<false>(p[0], p[1], p[2], p[3]);
+            ph[2 * nb + w / 2][2 * (w % 2)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+            ph[2 * nb + w / 2][2 * (w % 2) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *(u32x4*)(&Px[buf][pxoff + 16 * c]) = ph[c];
+        const i32x8 pb = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int o = troff + db * G::TDB;
+          acc[db] = mfma8<FDO, 0>(lds_op16x2(&Dt[buf][o], &Dt[buf][o + 32]), pb, acc[db]);
+        }
+      };
       if (need_mask)
-        body(std::true_type{}, std::true_type{});
+        dv_body(std::true_type{});
       else
-        body(std::true_type{}, std::false_type{});
-    } else {
-      if (need_mask)
-        body(std::false_type{}, std::true_type{});
-      else
-        body(std::false_type{}, std::false_type{});
+        dv_body(std::false_type{});
     }
+    b3 = b3n;
   }
+  // The last tile's dS: its P was written in the last step.
+  __syncthreads();
+  if (role_dk && prev_live) dk_finish((n_it - 1) & 1, b3 == 0 ? 2 : b3 - 1);
 
   if (AMAX && role_dk) {
     // One max per wave; non-negative floats order as their bit patterns.
