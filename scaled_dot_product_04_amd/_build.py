@@ -10,8 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
-SOURCES = ["sdpa_api.hip", "fwd_kernels.hip", "bwd_kernels.hip", "fp8_kernels.hip", "fp8_bwd_kernels.hip",
-           "decode_kernels.hip", "probe_kernels.hip"]
+SOURCES = ["sdpa_api.hip", "fwd_kernels.hip", "f32_kernels.hip", "bwd_kernels.hip", "fp8_kernels.hip",
+           "fp8_bwd_kernels.hip", "decode_kernels.hip", "probe_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for all device code. MFMA accumulators

@@ -462,101 +462,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   }
 }
 
-// fp32 I/O: one thread per query row, K/V tiles of 32 keys in LDS, fp32 FMA.
-template <int D, bool CAUSAL, bool MOD>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int n_qblk) {
-  constexpr int BN = 32;
-  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x % (a.b * a.h_q);
-  const int qb = n_qblk - 1 - blockIdx.x / (a.b * a.h_q);
-  const int bi = bh / a.h_q, hq = bh % a.h_q;
-  const int g = hq / (a.h_q / a.h_kv);
-  const int qblk0 = qb * 64;
-  const int my_q = qblk0 + tid;
-  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
-  const float* qp = (const float*)a.q + bi * a.qs.b + hq * a.qs.h;
-  const float* kp = (const float*)a.k + bi * a.ks.b + g * a.ks.h;
-  const float* vp = (const float*)a.v + bi * a.vs.b + g * a.vs.h;
-  const float sl2 = a.scale * kLog2e;
-
-  float qv[D], o[D];
-#pragma unroll
-  for (int d4 = 0; d4 < D; d4 += 4) {
-    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (my_q < L.lq) x = *(const f32x4*)(qp + (int64_t)my_q * a.qs.s + d4);
-    qv[d4] = x[0] * sl2;
-    qv[d4 + 1] = x[1] * sl2;
-    qv[d4 + 2] = x[2] * sl2;
-    qv[d4 + 3] = x[3] * sl2;
-    o[d4] = o[d4 + 1] = o[d4 + 2] = o[d4 + 3] = 0.f;
-  }
-  float m_run = -INFINITY, l_run = 0.f;
-  const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + 64, L.lq) + L.off)) : L.lk;
-  for (int k0 = 0; k0 < kv_end; k0 += BN) {
-    __syncthreads();
-    for (int c = tid; c < BN * D / 4; c += 64) {
-      const int r = c / (D / 4), d4 = 4 * (c % (D / 4));
-      f32x4 kx = f32x4{0.f, 0.f, 0.f, 0.f}, vx = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (k0 + r < L.lk) {
-        kx = *(const f32x4*)(kp + (int64_t)(k0 + r) * a.ks.s + d4);
-        vx = *(const f32x4*)(vp + (int64_t)(k0 + r) * a.vs.s + d4);
-      }
-      *(f32x4*)(&Ks[r * D + d4]) = kx;
-      *(f32x4*)(&Vs[r * D + d4]) = vx;
-    }
-    __syncthreads();
-    float s[BN];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < BN; ++jj) {
-      float acc = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) acc = fmaf(qv[dd], Ks[jj * D + dd], acc);
-      const int key = k0 + jj;
-      if (MOD) {  // (bias - slope * |i + off - j|) * log2e; acc is already in log2 units
-        const float bval = (a.mod.bias != nullptr && my_q < a.s_q)
-                               ? bias1<Bf16T>((const char*)a.mod.bias +
-                                                  (bi * a.mod.bb + hq * a.mod.bh + (int64_t)my_q * a.mod.bs) * 4,
-                                              1, key, a.s_kv)
-                               : 0.f;
-        const float slope = a.mod.slopes != nullptr ? a.mod.slopes[hq] : 0.f;
-        acc = fmaf(bval - slope * fabsf((float)(my_q + L.off - key)), kLog2e, acc);
-      }
-      if (key >= L.lk || (CAUSAL && key > my_q + L.off)) acc = -INFINITY;
-      s[jj] = acc;
-      mx = fmaxf(mx, acc);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    // m stays -inf while every score of the row is -inf: P = 0, nothing to rescale.
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float msub = m_new == -INFINITY ? 0.f : m_new;
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int dd = 0; dd < D; ++dd) o[dd] *= alpha;
-#pragma unroll
-    for (int jj = 0; jj < BN; ++jj) {
-      const float p = __builtin_amdgcn_exp2f(s[jj] - msub);
-      l_run += p;
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) o[dd] = fmaf(p, Vs[jj * D + dd], o[dd]);
-    }
-  }
-  if (my_q < a.s_q) {
-    // Rows past lq, and rows that see no key: O = 0, LSE = -inf.
-    const bool live = my_q < L.lq && l_run > 0.f;
-    const float inv = live ? 1.f / l_run : 0.f;
-    float* op = (float*)a.o + bi * a.os.b + hq * a.os.h + (int64_t)my_q * a.os.s;
-#pragma unroll
-    for (int d4 = 0; d4 < D; d4 += 4)
-      *(f32x4*)(op + d4) = f32x4{o[d4] * inv, o[d4 + 1] * inv, o[d4 + 2] * inv, o[d4 + 3] * inv};
-    if (a.lse != nullptr)
-      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  }
-}
-
 template <typename T, int D, int NW, int MOD, int KS = 1>
 hipError_t launch_mfma_dm(const FwdArgs& a, hipStream_t stream) {
   const int bm = 32 * NW / KS;
@@ -593,25 +498,6 @@ hipError_t launch_mfma_d(const FwdArgs& a, hipStream_t stream) {
   }
 }
 
-template <int D>
-hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
-  const int n_qblk = (a.s_q + 63) / 64;
-  const dim3 grid(n_qblk * a.b * a.h_q), block(64);
-  const bool mod = has_mod(a.mod);
-  if (a.causal) {
-    if (mod)
-      hipLaunchKernelGGL((fwd_f32_kernel<D, true, true>), grid, block, 0, stream, a, n_qblk);
-    else
-      hipLaunchKernelGGL((fwd_f32_kernel<D, true, false>), grid, block, 0, stream, a, n_qblk);
-  } else {
-    if (mod)
-      hipLaunchKernelGGL((fwd_f32_kernel<D, false, true>), grid, block, 0, stream, a, n_qblk);
-    else
-      hipLaunchKernelGGL((fwd_f32_kernel<D, false, false>), grid, block, 0, stream, a, n_qblk);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 // Up to 1024 keys the d = 128 forward runs 4-wave workgroups with 64-key tiles
@@ -628,10 +514,6 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, Io io, hipStream_t stream) {
   }
   if (a.d == 64) return launch_mfma_d<F16T, 64, 4>(a, stream);
   return small ? launch_mfma_d<F16T, 128, 4>(a, stream) : launch_mfma_d<F16T, 128, 8>(a, stream);
-}
-
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
-  return a.d == 64 ? launch_f32_d<64>(a, stream) : launch_f32_d<128>(a, stream);
 }
 
 }  // namespace sdpa
