@@ -140,11 +140,27 @@ __device__ __forceinline__ constexpr int key_of(int t, int h, int m) {
   return 16 * t + 8 * (m / 4) + 4 * h + (m % 4);
 }
 
-__device__ __forceinline__ float wave_max_halves(float x) {
-  // max with the lane 32 apart (the other half holding the same column)
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// Max / sum of x over lanes l and l ^ 32 (the two halves holding the same
+// accumulator column), in both lanes, through v_permlane32_swap (a VALU
+// exchange: no LDS traffic, no LDS wait). The swap of a register pair (a, b),
+// both holding x, leaves x of lanes 0..31 in both halves of a and x of lanes
+// 32..63 in both halves of b. It is written in assembly because the compiler's
+// builtin returns its first result for both outputs; the two wait states
+// before it are the ones the compiler itself puts between a VALU write and the
+// swap's read. Every lane of the wave must be active.
+__device__ __forceinline__ f32x2 halves_swap(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return f32x2{lo, hi};
 }
-__device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float wave_max_halves(float x) {
+  const f32x2 r = halves_swap(x);
+  return fmaxf(r.x, r.y);
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  const f32x2 r = halves_swap(x);
+  return r.x + r.y;
+}
 
 // Chunk swizzle of the row-major V tile: row r keeps its 16-byte chunk c at
 // position c ^ vswz<D>(r). The LDS serves a 64-lane 8-byte read in two passes

@@ -15,8 +15,11 @@
 // folded into the exp2 argument. The softmax weights p = exp(S - m) <= 1 are
 // quantised to e4m3 as p * scale_p for the second matmul O^T += V^T P^T (also
 // fp8 MFMA); the row sum l uses the unquantised fp32 p. O = O_acc * descale_v *
-// descale_p / l. The running max is kept exact (every increase rescales), so
-// p <= 1 and p * scale_p never exceeds the e4m3 range when scale_p <= 448.
+// descale_p / l. The running max moves (and O, l are rescaled) only when a
+// tile's row max exceeds it by more than kLazy8 (log2 units), so p <= 2^kLazy8;
+// the weights are quantised as p * scale_p * 2^-kLazy8, which stays within the
+// e4m3 range when scale_p <= 448. The factor cancels in O_acc / l, and the LSE
+// adds it back.
 //
 // Layout: one workgroup = 4 waves x 32 query rows; each lane owns one query
 // column of S^T. K tiles (64 keys) are staged row-major in LDS; V tiles are
@@ -37,6 +40,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // CU, one K/V staging for eight waves), 4 at d = 128 (three per CU).
 constexpr int fp8_waves(int d) { return d == 256 ? 8 : 4; }
 constexpr int kBN8 = 64;     // keys per tile (one 64-deep MFMA step of P V)
+// Lazy running max: a row's max is only moved when it grows by more than this
+// (log2 units). With an exact max, some row of a 32-row wave raises its max in
+// most tiles of a long row, and each raise rescaled O (64 multiplies per lane):
+// b2 h16 s8192 d128 causal 0.394 -> 0.363 ms, b4 h8 s8192 d256 1.118 -> 1.035
+// ms (same-box A/B).
+constexpr float kLazy8 = 2.f;
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 = e4m3 for both operands, unit E8M0 scales (127 = 2^0)
@@ -226,7 +235,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
     mx = wave_max_halves(mx) * sl2;
-    if (__any(mx > m_run)) {
+    if (__any(mx > m_run + kLazy8)) {
       const float m_new = fmaxf(m_run, mx);
       // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -237,10 +246,10 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
-    // p * scale_p = exp2(S * scale * log2e - m + log2(scale_p)) in fp32: its
-    // sum is l * scale_p; its e4m3 rounding is packed as the B operand, byte
-    // m = 16 nb + r of this lane half.
-    const float off = lsp - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
+    // p * scale_p * 2^-kLazy8 = exp2(S * scale * log2e - m + log2(scale_p) -
+    // kLazy8) in fp32: its sum is l * scale_p * 2^-kLazy8; its e4m3 rounding
+    // is packed as the B operand, byte m = 16 nb + r of this lane half.
+    const float off = lsp - kLazy8 - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
     uint32_t pw[8];
     float ls0, ls1;
 #pragma unroll
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
     }
   }
 
-  const float l_tot = wave_sum_halves(l_run);  // = l * scale_p
+  const float l_tot = wave_sum_halves(l_run);  // = l * scale_p * 2^-kLazy8
   // Rows past lq, and rows that see no key: O = 0, LSE = -inf.
   const bool live = my_q < L.lq && l_tot > 0.f;
   const float inv = live ? a.descale_v * a.descale_p * a.scale_p / l_tot : 0.f;
@@ -288,7 +297,8 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
         *(u32x2*)(op + d0) = w;
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + __log2f(l_tot) - lsp) * kLn2 : -INFINITY;
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] =
+          live ? (m_run + __log2f(l_tot) - lsp + kLazy8) * kLn2 : -INFINITY;
   }
 }
 

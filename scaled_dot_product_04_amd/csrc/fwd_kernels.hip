@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int grp = wave / RW, rw = wave - grp * RW;  // key group, row wave
   const int kg = grp * GBN;                         // the group's keys in a tile
@@ -138,24 +138,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
 
   // Staging map: thread owns 16-byte chunks (row r, chunk cc) of K and of V;
   // consecutive threads read consecutive chunks of a row from HBM. K rows are
-  // padded in LDS, V rows are swizzled. Byte offsets inside a tile are
-  // loop-invariant; tiles move the buffer base.
-  uint32_t koff[KCH], kdst[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / CH, cc = c % CH;
-    koff[i] = (uint32_t)(r * a.ks.s * 2 + cc * 16);
-    kdst[i] = r * KSTR + cc * 8;
-  }
-  uint32_t voff2[KCH], vdst2[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / CH, cc = c % CH;
-    voff2[i] = (uint32_t)(r * a.vs.s * 2 + cc * 16);
-    vdst2[i] = r * D + ((cc ^ vswz<D>(r)) * 8);
-  }
+  // padded in LDS, V rows are swizzled. Chunk i of a thread is row
+  // tid / CH + i * RS, chunk tid % CH: its LDS offset is the thread's base plus
+  // a constant, its global offset the base plus i row strides (recomputed per
+  // tile from an opaque copy, which keeps one register per tensor live
+  // instead of KCH). Tiles move the buffer base.
+  static_assert(NT % CH == 0, "whole rows per thread step");
+  constexpr int RS = NT / CH;  // rows between a thread's chunks
+  const int r0 = tid / CH, cc0 = tid % CH;
+  const uint32_t koff0 = (uint32_t)(r0 * a.ks.s * 2 + cc0 * 16);
+  const uint32_t voff0 = (uint32_t)(r0 * a.vs.s * 2 + cc0 * 16);
+  const uint32_t kstep = (uint32_t)(RS * a.ks.s * 2), vstep = (uint32_t)(RS * a.vs.s * 2);
+  // vswz depends on the row only through r % 4 (d = 128) or (r / 2) % 2
+  // (d = 64), which RS (a multiple of 4) leaves unchanged.
+  static_assert(RS % 4 == 0, "swizzle period");
+  const int kdst0 = r0 * KSTR + cc0 * 8;
+  const int vdst0 = r0 * D + ((cc0 ^ vswz<D>(r0)) * 8);
+  auto kdst = [&](int i) { return kdst0 + i * RS * KSTR; };
+  auto vdst = [&](int i) { return vdst0 + i * RS * D; };
   u32x4 vreg2[KCH];
   SwzLaneF<D> sl;
   sl.init(lane);
@@ -164,17 +164,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     // Rows at or past lk read as zero (never the caller's padding).
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
+    uint32_t ko = koff0, vo = voff0;
+    asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
+    for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, ko + i * kstep);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) vreg2[i] = buf_load16(vr, voff2[i]);
+    for (int i = 0; i < KCH; ++i) vreg2[i] = buf_load16(vr, vo + i * vstep);
   };
   // Registers -> LDS buffer.
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Ks[buf][kdst[i]]) = kreg[i];
+    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Ks[buf][kdst(i)]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Vs[buf][vdst2[i]]) = vreg2[i];
+    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Vs[buf][vdst(i)]) = vreg2[i];
   };
 
   // The tile loop. fast (no modifiers only): the weights of a tile are taken
@@ -231,9 +233,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
         // wave's keys get no weight at all.) A row whose max is key 0, like
         // causal row 0, gets the weight exp2(0) = 1 for it, as with an exact
         // max. The first key is accumulator register 0 of the lower half-wave.
-        const float s_key0 = sacc[0][0];
-        const float other = __shfl_xor(s_key0, 32, 64);
-        m_run = (h ? other : s_key0) * sc;
+        m_run = halves_swap(sacc[0][0]).x * sc;  // lane j's value in both halves
       }
       if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
 #pragma unroll
