@@ -15,18 +15,20 @@
 // folded into the exp2 argument. The softmax weights p = exp(S - m) <= 1 are
 // quantised to e4m3 as p * scale_p for the second matmul O^T += V^T P^T (also
 // fp8 MFMA); the row sum l uses the unquantised fp32 p. O = O_acc * descale_v *
-// descale_p / l. The running max moves (and O, l are rescaled) only when a
-// tile's row max exceeds it by more than kLazy8 (log2 units), so p <= 2^kLazy8;
-// the weights are quantised as p * scale_p * 2^-kLazy8, which stays within the
-// e4m3 range when scale_p <= 448. The factor cancels in O_acc / l, and the LSE
-// adds it back.
+// descale_p / l. The running max is kept exact (every increase rescales), so
+// p <= 1, p * scale_p never exceeds the e4m3 range when scale_p <= 448, and
+// the largest weight of a row is exactly scale_p: a running max that trails
+// the row max leaves that weight to e4m3 rounding (3 mantissa bits), which
+// on a row dominated by one late key moved O by up to 0.14.
 //
-// Layout: one workgroup = 4 waves x 32 query rows; each lane owns one query
-// column of S^T. K tiles (64 keys) are staged row-major in LDS; V tiles are
-// staged transposed, with the keys of each row permuted so that the 32 keys
-// one lane half contributes to a 64-deep MFMA step are one contiguous 32-byte
-// run (their order is the order of the accumulator registers the P operand
-// is packed from).
+// Layout: one workgroup = 4 waves x 32 query rows at d = 128, 8 at d = 256;
+// each lane owns one query column of S^T. K and V tiles (64 keys) are staged
+// row-major in LDS (V with swizzled 16-byte chunks); the V^T operand of the
+// second matmul is read with ds_read_b64_tr_b8, each lane's 32 keys in the
+// order of the accumulator registers the P operand is packed from. (Staging V
+// transposed through registers took 32 byte permutes per tile on the staging
+// threads: the transposed reads are 0.360 -> 0.332 ms at d = 128 causal
+// s8192 and 1.008 -> 0.987 ms at d = 256, same-box A/B.)
 #include "device_common.h"
 #include "sdpa_internal.h"
 
@@ -40,34 +42,34 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // CU, one K/V staging for eight waves), 4 at d = 128 (three per CU).
 constexpr int fp8_waves(int d) { return d == 256 ? 8 : 4; }
 constexpr int kBN8 = 64;     // keys per tile (one 64-deep MFMA step of P V)
-// Lazy running max: a row's max is only moved when it grows by more than this
-// (log2 units). With an exact max, some row of a 32-row wave raises its max in
-// most tiles of a long row, and each raise rescaled O (64 multiplies per lane):
-// b2 h16 s8192 d128 causal 0.394 -> 0.363 ms, b4 h8 s8192 d256 1.118 -> 1.035
-// ms (same-box A/B).
-constexpr float kLazy8 = 2.f;
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 = e4m3 for both operands, unit E8M0 scales (127 = 2^0)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// Byte transpose of a 4x4 block: in[r] holds bytes (r, 0..3); out[c] holds
-// bytes (0..3, c).
-__device__ __forceinline__ void transpose4x4_b8(const uint32_t in[4], uint32_t out[4]) {
-  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
-  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+// ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i % 8
+// of the 8-byte pieces addressed by lanes 2 k + i / 8 of the group, k = 0..7
+// (byte k of the result from piece k).
+__device__ __forceinline__ u32x2 ds_read_tr8(const uint8_t* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p)));
 }
 
+// Chunk swizzle of the row-major V tile (16-byte chunks): row r keeps chunk c
+// at position c ^ vswz8(r). The transposed reads of one pass (32 lanes) take a
+// 32-byte column segment of the 8 rows 16 u + {0..3, 8..11} (+4 in the other
+// half-wave); with 128- or 256-byte rows, rows of equal parity would share
+// banks, and the XOR (bits 1 and 3 of the row -> chunk bits 1 and 2) moves
+// the four rows of each parity to four different 32-byte bank groups.
+// Invariant under +16 rows.
+__device__ __forceinline__ int vswz8(int r) { return (((r >> 1) & 1) | ((r >> 2) & 2)) << 1; }
+
 template <int D, bool CAUSAL>
-// Occupancy: at d = 256 one 8-wave workgroup per CU (254 VGPRs, 74 KB LDS),
-// at d = 128 three 4-wave workgroups (168 VGPRs): a second (third) wave per
+// Occupancy: at d = 256 one 8-wave workgroup per CU (about 245 VGPRs, 66 KB
+// LDS), at d = 128 three 4-wave workgroups (about 165 VGPRs, 34 KB LDS each):
+// a second (third) wave per
 // SIMD hides the softmax VALU work behind the other waves' MFMAs. At d = 256
 // the 8 waves share one K/V staging, which also halves each thread's staging
 // registers: two 4-wave workgroups per CU spilled 10 VGPRs and took 1.27 ms
@@ -79,15 +81,13 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
   constexpr int kBM8 = 32 * kNW;
   constexpr int NT = 64 * kNW;
   constexpr int KSTR = D + 16;       // bytes per K row in LDS
-  constexpr int VSTR = kBN8 + 16;    // bytes per transposed V row in LDS
+  constexpr int VCPR = D / 16;       // 16-byte chunks per V row
   constexpr int NKS = D / 64;        // 64-deep contraction steps over d
   constexpr int NDB = D / 32;        // 32-wide output blocks over d
   constexpr int KCH = kBN8 * D / 16 / NT;   // 16-byte K chunks per thread
-  constexpr int VTOT = kBN8 * D / 64;       // 4-key x 16-column V blocks per tile
-  constexpr int VBL = (VTOT + NT - 1) / NT; // ... per thread
-  static_assert(KCH >= 1 && KCH * NT * 16 == kBN8 * D && (VTOT % NT == 0 || VTOT < NT), "tile map");
+  static_assert(KCH >= 1 && KCH * NT * 16 == kBN8 * D, "tile map");
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBN8 * KSTR];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][kBN8 * D];  // row-major, vswz8 chunks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -130,10 +130,8 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
   const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + kBM8, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kBN8 - 1) / kBN8;
 
-  // Staging map. K: 16-byte chunks (row r, chunk cc). V: blocks of 4 keys x 16
-  // columns, loaded as four 16-byte row pieces and written transposed.
+  // Staging map. K: 16-byte chunks (row r, chunk cc).
   constexpr int KCPR = D / 16;  // K chunks per row
-  constexpr int VCG = D / 16;   // V column groups of 16
   uint32_t koff[KCH], kdst[KCH];
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
@@ -142,26 +140,17 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
     koff[i] = (uint32_t)(r * a.ks.s + cc * 16);
     kdst[i] = r * KSTR + cc * 16;
   }
-  // At d = 256, block c is key group c % 16 of column group c / 16: the 64
-  // lanes of one transposed store then write 16 different 4-byte positions
-  // of only 4 rows (4 lanes per bank; with the column group fastest, the 16
-  // lanes of a key group share a bank). Same-box A/B, b4 h8 s8192: 1.85 ->
-  // 1.27 ms. At d = 128 the column group stays fastest: there the wider
-  // row-contiguous global loads of that order matter more (0.41 vs 0.42 ms).
-  uint32_t voff[VBL], vdst[VBL];
+  // V: 16-byte chunks like K, written row-major in the vswz8 layout.
+  uint32_t voff[KCH], vdst[KCH];
 #pragma unroll
-  for (int i = 0; i < VBL; ++i) {
+  for (int i = 0; i < KCH; ++i) {
     const int c = tid + NT * i;
-    const int kg = D == 256 ? c % 16 : c / VCG;  // 4-key group 0..15
-    const int cg = D == 256 ? c / 16 : c % VCG;
-    voff[i] = (uint32_t)((4 * kg) * a.vs.s + 16 * cg);
-    // key 4 kg = 32 blk + 8 gq + 4 hh  ->  position 32 hh + 16 blk + 4 gq
-    const int blk = kg >> 3, gq = (kg & 7) >> 1, hh = kg & 1;
-    vdst[i] = (16 * cg) * VSTR + 32 * hh + 16 * blk + 4 * gq;
+    const int r = c / VCPR, cc = c % VCPR;
+    voff[i] = (uint32_t)(r * a.vs.s + cc * 16);
+    vdst[i] = r * D + ((cc ^ vswz8(r)) * 16);
   }
   u32x4 kreg[KCH];
-  u32x4 vreg[VBL][4];
-  const uint32_t vrow = (uint32_t)a.vs.s;
+  u32x4 vreg[KCH];
   auto load_tile = [&](int k0) {
     // Rows at or past lk read as zero (never the caller's padding).
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 1));
@@ -169,28 +158,31 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
 #pragma unroll
     for (int i = 0; i < KCH; ++i) kreg[i] = buf_load16(kr, koff[i]);
 #pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      if (VTOT % NT != 0 && tid + NT * i >= VTOT) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[i][r] = buf_load16(vr, voff[i] + r * vrow);
-    }
+    for (int i = 0; i < KCH; ++i) vreg[i] = buf_load16(vr, voff[i]);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) *(u32x4*)(&Ks[buf][kdst[i]]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      if (VTOT % NT != 0 && tid + NT * i >= VTOT) continue;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {  // columns 4 w .. 4 w + 3 of the 16
-        const uint32_t rows[4] = {vreg[i][0][w], vreg[i][1][w], vreg[i][2][w], vreg[i][3][w]};
-        uint32_t cols[4];
-        transpose4x4_b8(rows, cols);
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) *(uint32_t*)(&Vt[buf][vdst[i] + (4 * w + c2) * VSTR]) = cols[c2];
-      }
-    }
+    for (int i = 0; i < KCH; ++i) *(u32x4*)(&Vs[buf][vdst[i]]) = vreg[i];
   };
+
+  // Lane offsets of the transposed V reads. The A operand of O^T += V^T P^T
+  // for output block db: lane (d row j, half h) holds the 32 keys whose P
+  // bytes it meets, byte m = key 16 (m / 8) + 8 ((m % 8) / 4) + 4 h + m % 4
+  // (the order P is packed in), as four ds_read_b64_tr_b8, read u giving bytes
+  // 8 u .. 8 u + 7. For that, lane l of 16-lane group G addresses the 8-byte
+  // piece of key row 16 u + 8 (k / 4) + 4 (G / 2) + k % 4, k = (l % 16) / 2, at
+  // columns 32 db + 16 (G % 2) + 8 (l % 2): the row is one base plus 16 u rows.
+  // (vswz8 only touches chunk bits 1-2, so blocks db and db + 4 of d = 256
+  // are 128 bytes apart.)
+  int vtr[4];
+  {
+    const int G = lane >> 4, L = lane & 15, k = L >> 1;
+    const int r0 = 8 * (k >> 2) + 4 * (G >> 1) + (k & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vtr[db] = r0 * D + (((2 * db + (G & 1)) ^ vswz8(r0)) * 16) + 8 * (L & 1);
+  }
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -235,7 +227,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
     mx = wave_max_halves(mx) * sl2;
-    if (__any(mx > m_run + kLazy8)) {
+    if (__any(mx > m_run)) {
       const float m_new = fmaxf(m_run, mx);
       // A row that has seen no visible key yet keeps m = -inf (and O = l = 0).
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -246,10 +238,10 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
-    // p * scale_p * 2^-kLazy8 = exp2(S * scale * log2e - m + log2(scale_p) -
-    // kLazy8) in fp32: its sum is l * scale_p * 2^-kLazy8; its e4m3 rounding
-    // is packed as the B operand, byte m = 16 nb + r of this lane half.
-    const float off = lsp - kLazy8 - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
+    // p * scale_p = exp2(S * scale * log2e - m + log2(scale_p)) in fp32: its
+    // sum is l * scale_p; its e4m3 rounding is packed as the B operand, byte
+    // m = 16 nb + r of this lane half.
+    const float off = lsp - (m_run == -INFINITY ? 0.f : m_run);  // all -inf scores: P = 0
     uint32_t pw[8];
     float ls0, ls1;
 #pragma unroll
@@ -273,14 +265,15 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
     // O^T += V^T P^T over the 64 keys of the tile.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* vr = &Vt[buf][(db * 32 + j) * VSTR + 32 * h];
-      const u32x4 lo = *(const u32x4*)vr, hi = *(const u32x4*)(vr + 16);
-      const i32x8 va = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint8_t* vr = &Vs[buf][vtr[db & 3] + 128 * (db >> 2)];
+      const u32x2 r0 = ds_read_tr8(vr), r1 = ds_read_tr8(vr + 16 * D), r2 = ds_read_tr8(vr + 32 * D),
+                  r3 = ds_read_tr8(vr + 48 * D);
+      const i32x8 va = i32x8{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, (int)r3.x, (int)r3.y};
       oacc[db] = mfma_fp8(va, pb, oacc[db]);
     }
   }
 
-  const float l_tot = wave_sum_halves(l_run);  // = l * scale_p * 2^-kLazy8
+  const float l_tot = wave_sum_halves(l_run);  // = l * scale_p
   // Rows past lq, and rows that see no key: O = 0, LSE = -inf.
   const bool live = my_q < L.lq && l_tot > 0.f;
   const float inv = live ? a.descale_v * a.descale_p * a.scale_p / l_tot : 0.f;
@@ -297,8 +290,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
         *(u32x2*)(op + d0) = w;
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] =
-          live ? (m_run + __log2f(l_tot) - lsp + kLazy8) * kLn2 : -INFINITY;
+      a.lse[((int64_t)bi * a.h_q + hq) * a.s_q + my_q] = live ? (m_run + __log2f(l_tot) - lsp) * kLn2 : -INFINITY;
   }
 }
 

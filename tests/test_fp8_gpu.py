@@ -9,6 +9,7 @@ small), and LSE within 1e-3 relative (it does not involve the quantised P)."""
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import sdpa_inputs
@@ -65,3 +66,33 @@ def test_fp8_hd256_full_size_sampled():
     rows = sorted(set([0, 1, 63, 64, 4095, w.s_q - 1] + [int(x) for x in rng.integers(0, w.s_q, 40)]))
     o_ref, lse_ref = oracle_fwd(w, ins, heads=heads, rows=np.array(rows))
     _check(w, o, lse, o_ref, lse_ref, rows=rows)
+
+
+@pytest.mark.parametrize("beta", [14.7, -7.0])
+def test_fp8_late_dominant_key(beta):
+    """One key of a row, in a later 64-key tile, scores 0.4-2.7 (log2 units) above (beta > 0)
+    or below (beta < 0) the first tile's max; V is +4 on key 0 and -4 on that key. With the
+    exact running max the larger of the two weights is exactly scale_p; a max that trails the
+    row max (moved only past a threshold) left it to e4m3 rounding and O off by up to 0.14.
+    Scores are scale * alpha_i * b_j on one coordinate: key 0 gives 0, key 150 gives
+    beta * scale * alpha_i, every other key at most -8.8 nats."""
+    b, h, s, d = 1, 1, 256, 128
+    w = Workload("fp8_late_max", b, h, h, s, s, d, "fp8", "bf16", False, 1 / math.sqrt(d), "bhsd", 0)
+    q = torch.zeros(b, h, s, d)
+    k = torch.zeros(b, h, s, d)
+    alpha = 0.5 + torch.arange(s, dtype=torch.float32) / s
+    q[0, 0, :, 0] = alpha
+    k[0, 0, :, 0] = -200.0
+    k[0, 0, 0, 0] = 0.0
+    k[0, 0, 150, 0] = beta
+    v = torch.randn(b, h, s, d, generator=torch.Generator().manual_seed(5)) * 0.1
+    v[0, 0, 0, :] = 4.0
+    v[0, 0, 150, :] = -4.0
+    ins = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        ins[name], ins["descale_" + name] = sdpa_inputs.quantize_fp8(x)
+    ins["scale_p"] = sdpa_inputs.FP8_MAX
+    ins["descale_p"] = 1.0 / sdpa_inputs.FP8_MAX
+    o, lse = gpu_fwd(w, to_gpu(ins))
+    o_ref, lse_ref = oracle_fwd(w, ins)
+    _check(w, o, lse, o_ref, lse_ref)
