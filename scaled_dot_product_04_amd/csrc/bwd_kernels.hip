@@ -168,7 +168,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   __shared__ __attribute__((aligned(16))) float lse2s[kQTile];
   __shared__ __attribute__((aligned(16))) float dels[kQTile];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int n_slots = a.b * a.h_kv * n_split;
   // Linear id -> (key block, slot); causal: key block 0 (the most query tiles) first.
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int rank = blockIdx.x / bh_total;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(64 * kNW32) void fwd_f32_mfma_kernel(FwdArgs a, int
   __shared__ __attribute__((aligned(16))) float Ks[kBN32 * KSTR];
   __shared__ __attribute__((aligned(16))) float Vt[D * VSTR];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int bh = blockIdx.x % bh_total;

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
   __shared__ __attribute__((aligned(16))) float lse2s[2][kT8];
   __shared__ __attribute__((aligned(16))) float dels[3][kT8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const bool role_dk = wu >= 4;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dq_kernel(BwdArgs a, int n_qblk)
   __shared__ __attribute__((aligned(16))) uint8_t Vr[2][G::ROW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Kt[2][G::T_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int rank = blockIdx.x / bh_total;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * fp8_waves(D), D == 256 ? 1 : 3) void fwd_fp8_k
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2][kBN8 * D];  // row-major, vswz8 chunks
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
   const int bh_total = a.b * a.h_q;
   const int rank = blockIdx.x / bh_total;
