@@ -36,8 +36,8 @@
 //     stream through LDS (K row-major and transposed, V row-major). It also
 //     writes D = rowsum(dO * O) for the second kernel.
 //  2. dK/dV: key-stationary (8 waves x 32 keys; the wave's K and V rows stay in
-//     registers); 64-row Q / dO tiles, row-major and transposed, stream
-//     through LDS. Query-head groups that would underfill the GPU are split
+//     registers); 64-row Q / dO tiles stream through LDS row-major and are
+//     also read transposed (ds_read_b64_tr_b8). Query-head groups that would underfill the GPU are split
 //     and reduced as in the 16-bit backward.
 #include <type_traits>
 
@@ -86,54 +86,31 @@ __device__ __forceinline__ constexpr int pi_pos(int q) {
   return 32 * (q >> 5) + 8 * ((q >> 2) & 3) + 4 * ((q >> 4) & 1) + (q & 3);
 }
 
-// Byte transpose of a 4x4 block: in[r] holds bytes (r, 0..3); out[c] holds
-// bytes (0..3, c).
-__device__ __forceinline__ void tr4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t out[4]) {
-  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
-// LDS geometry of one 64-row fp8 tile of D columns.
-//  Row-major (A operand of the score products): pitch D + 16 bytes, row q at
-//    position pi_pos(q); 16 lanes reading one 16-byte column chunk of 16
-//    consecutive positions hit 16 distinct 4-bank groups (36 dwords apart).
-//  Transposed (A operand of dV, dK, dQ): row c (column c of the tile) holds
-//    the tile's 64 rows in order; pitch 80 bytes, plus 16 bytes per 16 rows so
-//    that the staging stores of one instruction (rows 8 apart) spread over
-//    all banks.
+// LDS geometry of one 64-row fp8 tile of D columns, row-major (the A operand
+// of the score products, and through transposed reads of the dV, dK and dQ
+// products): pitch D + 16 bytes, row q at position pi_pos(q); 16 lanes
+// reading one 16-byte column chunk of 16 consecutive positions hit 16
+// distinct 4-bank groups (36 dwords apart).
 template <int D>
 struct Geo8 {
   static constexpr int RSTR = D + 16;
   static constexpr int ROW_BYTES = kT8 * RSTR;
-  static constexpr int TSTR = kT8 + 16;
-  static constexpr int T_BYTES = D * TSTR + 16 * (D / 16);
-  static __device__ __forceinline__ int trow(int c) { return c * TSTR + 16 * (c >> 4); }
-  // trow(32 db + c) - trow(c) for c < 32
-  static constexpr int TDB = 32 * TSTR + 32;
   static constexpr int BPT = (kT8 / 4) * (D / 8);  // 4-row x 8-byte blocks per tile
 };
 
 // One 4-row x 8-byte block (rows 4 rg .. 4 rg + 3, bytes 8 cg .. 8 cg + 7) of
 // a 64-row fp8 tile in flight, loaded with buffer loads (rows past the end
-// read as zero), stored row-major and optionally transposed.
+// read as zero) and stored row-major.
 template <int D>
 struct Blk8 {
   typedef Geo8<D> G;
   u32x2 r[4];
   uint32_t goff;  // byte offset of the block's first row, relative to the tile's first row
   int rdst;       // row-major LDS offset of its first row (pi_pos(4 rg + e) = pi_pos(4 rg) + e)
-  int tdst;       // transposed LDS offset of its column 8 cg, row 4 rg
   __device__ __forceinline__ void init(int t, int64_t stride) {
     const int rg = t / (D / 8), cg = t % (D / 8);
     goff = (uint32_t)(4 * rg * stride + 8 * cg);
     rdst = pi_pos(4 * rg) * G::RSTR + 8 * cg;
-    tdst = G::trow(8 * cg) + 4 * rg;
   }
   __device__ __forceinline__ void load(const uint8_t* tile0, int row0, int n_rows, int64_t stride) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile0, tile_bytes(row0, n_rows, stride, D, 1));
@@ -145,25 +122,38 @@ struct Blk8 {
 #pragma unroll
     for (int e = 0; e < 4; ++e) *(u32x2*)(&tile[rdst + e * G::RSTR]) = r[e];
   }
-  __device__ __forceinline__ void store_cols(uint8_t* tileT) const {
-    uint32_t c[4];
-    tr4x4(r[0].x, r[1].x, r[2].x, r[3].x, c);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) *(uint32_t*)(&tileT[tdst + cc * G::TSTR]) = c[cc];
-    tr4x4(r[0].y, r[1].y, r[2].y, r[3].y, c);
-    // columns 4..7 of the block: rows 8 cg + 4 .. + 7 (same 16-row group as 8 cg)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) *(uint32_t*)(&tileT[tdst + (4 + cc) * G::TSTR]) = c[cc];
-  }
 };
 
 __device__ __forceinline__ i32x8 lds_op32(const uint8_t* p) {
   const u32x4 lo = *(const u32x4*)p, hi = *(const u32x4*)(p + 16);
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
-__device__ __forceinline__ i32x8 lds_op16x2(const uint8_t* p0, const uint8_t* p1) {
-  const u32x4 lo = *(const u32x4*)p0, hi = *(const u32x4*)p1;
-  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+// ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i % 8
+// of the 8-byte pieces addressed by lanes 2 k + i / 8 of the group, k = 0..7
+// (byte k of the result from piece k).
+__device__ __forceinline__ u32x2 ds_read_tr8(const uint8_t* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p)));
+}
+
+// Transposed A operand (column block of a row-major tile, contraction over the
+// tile's 64 rows) read straight from the row-major tile: lane (column j, half
+// h) gets the rows 16 h .. 16 h + 15 and 32 + 16 h .. 32 + 16 h + 15 in order,
+// which sit at positions pi_pos() = 16 u + 8 (k / 4) + 4 h + k % 4 for byte
+// 8 u + k. Lane l of 16-lane group G addresses position 8 (k / 4) +
+// 4 (G / 2) + k % 4 (k = (l % 16) / 2) at columns 16 (G % 2) + 8 (l % 2) of
+// the block (tr_lane_off); the four reads are 16 positions apart.
+template <int D>
+__device__ __forceinline__ int tr_lane_off(int lane) {
+  const int G = lane >> 4, L = lane & 15, k = L >> 1;
+  return (8 * (k >> 2) + 4 * (G >> 1) + (k & 3)) * Geo8<D>::RSTR + 16 * (G & 1) + 8 * (L & 1);
+}
+template <int D>
+__device__ __forceinline__ i32x8 lds_tr_op(const uint8_t* p) {
+  constexpr int P16 = 16 * Geo8<D>::RSTR;
+  const u32x2 r0 = ds_read_tr8(p), r1 = ds_read_tr8(p + P16), r2 = ds_read_tr8(p + 2 * P16), r3 = ds_read_tr8(p + 3 * P16);
+  return i32x8{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, (int)r3.x, (int)r3.y};
 }
 
 // ---------------------------------------------------------------------------
@@ -181,8 +171,10 @@ __device__ __forceinline__ i32x8 lds_op16x2(const uint8_t* p0, const uint8_t* p1
 // wave holds one accumulator set (64 registers), the exponentials are taken
 // once, and one barrier per tile still orders everything: P(t) is written
 // before the barrier that starts step t + 1, where the dK wave reads it. The
-// Q^T tile and D values stay one step longer (three buffers). Masked scores
-// give P = 0, hence dS = 0: the dK wave needs no mask.
+// Q tile and D values stay one step longer (three buffers). The transposed
+// operands (Q^T of dK, dO^T of dV) are read from the row-major tiles with
+// ds_read_b64_tr_b8. Masked scores give P = 0, hence dS = 0: the dK wave
+// needs no mask.
 template <int D, bool CAUSAL, bool DO_E5M2, bool DS_E5M2, bool AMAX>
 __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_split, float* part) {
   typedef Geo8<D> G;
@@ -193,10 +185,10 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
   // P exchange: per key slice, 64 lanes x 32 fp16 (64 bytes) at an 80-byte
   // pitch (16 lanes storing one 16-byte piece each hit distinct 4-bank groups).
   constexpr int PXP = 80, PXS = 64 * PXP;
-  __shared__ __attribute__((aligned(16))) uint8_t Qr[2][G::ROW_BYTES];
+  // Row-major Q (three deep: the dK wave reads a tile's Q^T one step after
+  // its S) and dO tiles; the transposed operands are read from them.
+  __shared__ __attribute__((aligned(16))) uint8_t Qr[3][G::ROW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Dr[2][G::ROW_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Dt[2][G::T_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Qt[3][G::T_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Px[2][4 * PXS];
   __shared__ __attribute__((aligned(16))) float lse2s[2][kT8];
   __shared__ __attribute__((aligned(16))) float dels[3][kT8];
@@ -292,13 +284,10 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
     }
   };
   auto store_tile = [&](int b2, int b3) {
-    if (st_q) {
-      blk.store_rows(Qr[b2]);
-      blk.store_cols(Qt[b3]);
-    } else if (st_d) {
+    if (st_q)
+      blk.store_rows(Qr[b3]);
+    else if (st_d)
       blk.store_rows(Dr[b2]);
-      blk.store_cols(Dt[b2]);
-    }
     if (tid < kT8) {
       // A row that sees no key has LSE = -inf and every score masked; 0 keeps
       // exp2(-inf - lse) at 0 instead of NaN.
@@ -308,14 +297,14 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
   };
 
   // Per-lane LDS offsets: A-operand row j of each 32-row block, the
-  // transposed rows 32 db + j (two 16-row runs, 16 h and 32 + 16 h), and this
-  // lane's P exchange slot.
+  // transposed reads (tr_lane_off; column block db 32 db bytes further), and
+  // this lane's P exchange slot.
   const int rowoff = j * G::RSTR + 32 * h;
-  const int troff = G::trow(j) + 16 * h;
+  const int troff = tr_lane_off<D>(lane);
   const int pxoff = kw * PXS + lane * PXP;
 
-  // dK wave: dS and dK for the tile whose dP is in dph, P in Px[pb], Q^T in
-  // Qt[b3], D in dels[b3].
+  // dK wave: dS and dK for the tile whose dP is in dph, P in Px[pb], Q in
+  // Qr[b3], D in dels[b3].
   auto dk_finish = [&](int pb, int b3) __attribute__((always_inline)) {
     // Read as eight fp16 values per 16 bytes. (Bit-casting single 32-bit
     // elements of a 4 x u32 vector to two fp16 values and converting them has
@@ -343,10 +332,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
       }
     const i32x8 sb = i32x8{(int)sk[0], (int)sk[1], (int)sk[2], (int)sk[3], (int)sk[4], (int)sk[5], (int)sk[6], (int)sk[7]};
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int o = troff + db * G::TDB;
-      acc[db] = mfma8<0, FDS>(lds_op16x2(&Qt[b3][o], &Qt[b3][o + 32]), sb, acc[db]);
-    }
+    for (int db = 0; db < NDB; ++db) acc[db] = mfma8<0, FDS>(lds_tr_op<D>(&Qr[b3][troff + 32 * db]), sb, acc[db]);
   };
 
   if (n_it > 0) {
@@ -397,7 +383,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
           f32x16 s = f32x16{};
 #pragma unroll
           for (int t = 0; t < NKS; ++t)
-            s = mfma8<0, 0>(lds_op32(&Qr[buf][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], s);
+            s = mfma8<0, 0>(lds_op32(&Qr[b3][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], s);
           if (MASKED) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -420,10 +406,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
         for (int c = 0; c < 4; ++c) *(u32x4*)(&Px[buf][pxoff + 16 * c]) = ph[c];
         const i32x8 pb = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int o = troff + db * G::TDB;
-          acc[db] = mfma8<FDO, 0>(lds_op16x2(&Dt[buf][o], &Dt[buf][o + 32]), pb, acc[db]);
-        }
+        for (int db = 0; db < NDB; ++db) acc[db] = mfma8<FDO, 0>(lds_tr_op<D>(&Dr[buf][troff + 32 * db]), pb, acc[db]);
       };
       if (need_mask)
         dv_body(std::true_type{});
@@ -483,7 +466,6 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dq_kernel(BwdArgs a, int n_qblk)
   constexpr int FDO = DO_E5M2 ? 1 : 0, FDS = DS_E5M2 ? 1 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t Kr[2][G::ROW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Vr[2][G::ROW_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Kt[2][G::T_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
@@ -564,12 +546,12 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dq_kernel(BwdArgs a, int n_qblk)
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
   const int rowoff = j * G::RSTR + 32 * h;
-  const int troff = G::trow(j) + 16 * h;
+  const int troff = tr_lane_off<D>(lane);  // K^T reads from the row-major K tile
 
   const int kv_end = qblk0 >= L.lq ? 0 : CAUSAL ? max(0, min(L.lk, min(qblk0 + kRows8, L.lq) + L.off)) : L.lk;
   const int n_tiles = (kv_end + kT8 - 1) / kT8;
-  // Staging: waves [0, BPT / 64) carry blocks of the K tile (row-major and
-  // transposed), waves [4, 4 + BPT / 64) blocks of the V tile (row-major);
+  // Staging: waves [0, BPT / 64) carry blocks of the K tile, waves [4, 4 +
+  // BPT / 64) blocks of the V tile (both row-major);
   // chosen per wave so that the buffer descriptor stays uniform.
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const bool st_k = wu < G::BPT / 64, st_v = wu >= 4 && wu - 4 < G::BPT / 64;
@@ -581,12 +563,10 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dq_kernel(BwdArgs a, int n_qblk)
     if (st_k || st_v) blk.load(stage_base + (int64_t)k0 * stage_s, k0, L.lk, stage_s);
   };
   auto store_tile = [&](int buf) {
-    if (st_k) {
+    if (st_k)
       blk.store_rows(Kr[buf]);
-      blk.store_cols(Kt[buf]);
-    } else if (st_v) {
+    else if (st_v)
       blk.store_rows(Vr[buf]);
-    }
   };
   if (n_tiles > 0) {
     load_tile(0);
@@ -635,8 +615,7 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dq_kernel(BwdArgs a, int n_qblk)
     // dQ^T += K^T dS^T over the tile's 64 keys.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      dq[db] = mfma8<0, FDS>(lds_op16x2(&Kt[buf][troff + db * G::TDB], &Kt[buf][troff + db * G::TDB + 32]), sb,
-                             dq[db]);
+      dq[db] = mfma8<0, FDS>(lds_tr_op<D>(&Kr[buf][troff + 32 * db]), sb, dq[db]);
   }
   if (my_q < a.s_q) {
     uint16_t* dqp = (uint16_t*)a.dq + bi * a.dqs.b + hq * a.dqs.h + (int64_t)my_q * a.dqs.s;
