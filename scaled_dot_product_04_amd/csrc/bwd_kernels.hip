@@ -25,6 +25,9 @@
 //     B operands of dV^T += dO^T P and dK^T += Q^T dS.
 //     When a GQA/MQA group would leave the GPU underfilled, the group's query
 //     heads are split over several workgroups that write fp32 partials.
+//     At d = 128 without score modifiers the same block runs as 4 waves of
+//     64 keys (bwd_dkdv64_kernel): one wave per SIMD, AGPR accumulators, and
+//     each LDS operand read feeding two MFMAs.
 //  3. reduce: sums the partials of the splits in a fixed order.
 #include "device_common.h"
 #include "sdpa_internal.h"
@@ -420,6 +423,306 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (unrolled at
+// compile time, so array indices derived from i stay in registers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// MFMA with its accumulator in AGPRs. The kernels of this file are compiled
+// with VGPR accumulators; this form keeps a long-lived accumulator out of the
+// 256 architectural VGPRs at one wave per SIMD (512 registers), and leaves
+// the VGPRs to the VALU work that runs beside the matrix core. The two wait
+// states cover a VALU write of an operand just before (the compiler does not
+// track hazards into inline assembly); readers of the accumulators must wait
+// for the last MFMA (mfma_acc_drain).
+template <typename T>
+__device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b);
+template <>
+__device__ __forceinline__ void mfma_acc<Bf16T>(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <>
+__device__ __forceinline__ void mfma_acc<F16T>(f32x16& c, f16x8 a, f16x8 b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 24 wait states: more than an MFMA result needs before a VALU or
+// v_accvgpr_read reads it. The accumulators pass through empty statements
+// ordered after the wait, so that no read of them moves above it (without
+// them the compiler hoisted the epilogue's AGPR reads over the wait).
+template <int N>
+__device__ __forceinline__ void mfma_acc_drain(f32x16 (&a0)[N], f32x16 (&a1)[N], f32x16 (&a2)[N], f32x16 (&a3)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    asm volatile("" : "+a"(a0[i]));
+    asm volatile("" : "+a"(a1[i]));
+    asm volatile("" : "+a"(a2[i]));
+    asm volatile("" : "+a"(a3[i]));
+  }
+}
+
+// KV-stationary dK/dV at d = 128 without score modifiers, one wave per SIMD.
+// A workgroup has 4 waves and the same 256-key block as bwd_dkdv_kernel, but
+// wave w owns 64 keys (two 32-key halves): every Q, dO row operand and every
+// Q^T, dO^T transposed operand read from LDS feeds two MFMAs, one per half,
+// and the dK^T / dV^T accumulators (256 registers) live in AGPRs, where the
+// vector work of the same wave can issue beside the MFMAs that update them.
+// With one wave per SIMD nothing hides a pause, so the tile body is a fixed
+// slot schedule (four phases of 16 MFMAs, operands read four slots ahead).
+// Same-box A/B at b2 h16 s8192 d128 causal: backward 1.849 -> 1.784 ms.
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_split, float* part) {
+  typedef typename T::vec8 V8;
+  constexpr int D = 128, NKS = D / 16, NDB = D / 32;
+  constexpr int NT = 256;
+  constexpr int CH = D / 8;
+  constexpr int KVC = kKvBlock * CH / NT;
+  constexpr int QCH = kQTile * CH;
+  constexpr int QPT = QCH / NT;
+  static_assert(KVC * NT == kKvBlock * CH && QPT * NT == QCH, "tile / thread mismatch");
+  // K/V block as in bwd_dkdv_kernel: row r = K row r, V row r, 16 bytes of padding.
+  constexpr int KVP = 2 * D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t KV[kKvBlock * KVP];
+  __shared__ __attribute__((aligned(16))) uint16_t QD[2 * kQTile * D];
+  uint16_t* const Qs = QD;
+  uint16_t* const Ds_ = QD + kQTile * D;
+  __shared__ __attribute__((aligned(16))) float nlse2s[kQTile];  // -LSE * log2 e
+  __shared__ __attribute__((aligned(16))) float dels[kQTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int j = lane & 31, h = lane >> 5;
+  const int n_slots = a.b * a.h_kv * n_split;
+  const int kb = blockIdx.x / n_slots;
+  const int slot = xcd_slot(blockIdx.x - kb * n_slots, n_slots, n_split);
+  const int sp = slot % n_split;
+  const int bg = slot / n_split;
+  const int g = bg % a.h_kv, bi = bg / a.h_kv;
+  const int G = a.h_q / a.h_kv, Gs = G / n_split;
+  const BatchLens L = batch_lens(a.seq_q, a.seq_kv, bi, a.s_q, a.s_kv, CAUSAL, a.bottom_right);
+
+  const int kw0 = kb * kKvBlock + wave * 64;  // this wave's keys: kw0 .. kw0 + 63
+  const int key0 = kw0 + j, key1 = key0 + 32;
+  const uint16_t* kp = (const uint16_t*)a.k + bi * a.ks.b + g * a.ks.h;
+  const uint16_t* vp = (const uint16_t*)a.v + bi * a.vs.b + g * a.vs.h;
+  {
+    const int k0 = kb * kKvBlock;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
+#pragma unroll
+    for (int i = 0; i < KVC; ++i) {
+      const int c = tid + NT * i;
+      const int r = c / CH, cc = c % CH;
+      const int dst = r * KVP + cc * 8;
+      *(u32x4*)(&KV[dst]) = buf_load16(kr, (uint32_t)(r * a.ks.s * 2 + cc * 16));
+      *(u32x4*)(&KV[dst + D]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
+    }
+  }
+  f32x16 dk0[NDB], dk1[NDB], dv0[NDB], dv1[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dk0[i] = dk1[i] = dv0[i] = dv1[i] = f32x16{};
+  const float sl2 = a.scale * kLog2e;
+  const int n_qt = (L.lq + kQTile - 1) / kQTile;
+  const int qt0 = CAUSAL ? min(n_qt, max(0, kb * kKvBlock - L.off) / kQTile) : 0;
+  const int nq = kb * kKvBlock >= L.lk ? 0 : n_qt - qt0;
+  const int n_it = Gs * nq;
+  const int hq_base = g * G + sp * Gs;
+
+  int rowoff_q[NKS];
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) rowoff_q[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
+  const int kvoff = (wave * 64 + j) * KVP + 8 * h;  // half 1: + 32 rows, an immediate
+  TrLaneB<D> trl;
+  trl.init(lane);
+
+  uint32_t qoff[QPT], doff[QPT];
+  int sdst[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int c = tid + NT * i, sr = c / CH, scc = c % CH;
+    qoff[i] = (uint32_t)(sr * a.qs.s * 2 + scc * 16);
+    doff[i] = (uint32_t)(sr * a.dos.s * 2 + scc * 16);
+    sdst[i] = sr * D + ((scc ^ bswz<D>(sr)) * 8);
+  }
+  u32x4 qreg[QPT], dreg[QPT];
+  float lreg = 0.f, creg = 0.f;
+  bool lvalid = false;
+  auto load_tile = [&](int it) {
+    const int hq = hq_base + it / nq;
+    const int q0 = (qt0 + it % nq) * kQTile;
+    const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h + (int64_t)q0 * a.qs.s;
+    const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)q0 * a.dos.s;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2));
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop, tile_bytes(q0, L.lq, a.dos.s, D, 2));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      qreg[i] = buf_load16(qr, qoff[i]);
+      dreg[i] = buf_load16(dr, doff[i]);
+    }
+    if (tid < kQTile) {
+      const int qi = q0 + tid;
+      lvalid = qi < L.lq;
+      const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + min(qi, L.lq - 1);
+      lreg = a.lse[row];
+      creg = a.delta[row];
+    }
+  };
+
+  if (n_it > 0) load_tile(0);
+  for (int it = 0; it < n_it; ++it) {
+    const int q0 = (qt0 + it % nq) * kQTile;
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      *(u32x4*)(&Qs[sdst[i]]) = qreg[i];
+      *(u32x4*)(&Ds_[sdst[i]]) = dreg[i];
+    }
+    if (tid < kQTile) {
+      nlse2s[tid] = (lvalid && lreg != -INFINITY) ? -lreg * kLog2e : 0.f;
+      dels[tid] = lvalid ? creg : 0.f;
+    }
+    if (it + 1 < n_it) load_tile(it + 1);
+    __syncthreads();  // this tile is in LDS
+    // A tile whose queries all precede this wave's keys is computed anyway,
+    // fully masked (it adds zeros): the SIMD has no other wave to give the
+    // time to, and a branch around the accumulation makes the register
+    // allocator move the AGPR accumulators through VGPRs.
+
+    // Four phases of 16 MFMA slots each; a scheduling fence closes every
+    // slot, so the vector work placed in a slot issues beside that slot's
+    // MFMA, and every LDS operand is read kLA slots before its MFMA:
+    //   A: S = Q K^T (both key halves share each Q read)
+    //   B: dP = dO V^T, beside it P = exp2(S scale log2 e - LSE log2 e)
+    //   C: dV^T += dO^T P (AGPR accumulators), beside it dS = P (dP - D)
+    //   D: dK^T += Q^T dS
+    constexpr int kLA = 4;
+    const bool need_mask = (q0 + kQTile > L.lq) || (kw0 + 64 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 63);
+    f32x16 sc[2] = {f32x16{}, f32x16{}}, dpc[2] = {f32x16{}, f32x16{}};
+    V8 ra[8], rb[2][8];   // phase A / B row operands: Q or dO (shared), K or V per half
+    f32x4 nl4[4], d4[4];  // -LSE log2 e and D of the lane's 16 query rows
+    float pf[2][16];
+    uint32_t pk[2][8], sk[2][8];
+    // Row-operand reads of slot m of phases A (m < 16) and B (m >= 16).
+    auto read_ab = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 32) {
+        constexpr int t = (m & 15) >> 1, hf = m & 1;
+        const uint16_t* tile = m < 16 ? Qs : Ds_;
+        const int kv = kvoff + (m < 16 ? 0 : D) + (hf ? 32 * KVP : 0) + 16 * t;
+        if constexpr (hf == 0) ra[t] = *(const V8*)(&tile[rowoff_q[t]]);
+        rb[hf][t] = *(const V8*)(&KV[kv]);
+      }
+    };
+    static_for<kLA>([&](auto mc) { read_ab(mc); });
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) nl4[r4] = *(const f32x4*)(&nlse2s[8 * r4 + 4 * h]);
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
+      sc[hf] = T::mfma(ra[t], rb[hf][t], sc[hf]);
+      read_ab(std::integral_constant<int, m + kLA>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + acc_row(r, h);
+        if (qi >= L.lq || key0 >= L.lk || (CAUSAL && key0 > qi + L.off)) sc[0][r] = -INFINITY;
+        if (qi >= L.lq || key1 >= L.lk || (CAUSAL && key1 > qi + L.off)) sc[1][r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) d4[r4] = *(const f32x4*)(&dels[8 * r4 + 4 * h]);
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
+      dpc[hf] = T::mfma(ra[t], rb[hf][t], dpc[hf]);
+      read_ab(std::integral_constant<int, m + 16 + kLA>{});
+      // P: two weights per slot, half ph, elements 2 w and 2 w + 1.
+      constexpr int ph = m >> 3, w = m & 7, r = 2 * w;
+      pf[ph][r] = __builtin_amdgcn_exp2f(fmaf(sc[ph][r], sl2, nl4[r >> 2][r & 3]));
+      pf[ph][r + 1] = __builtin_amdgcn_exp2f(fmaf(sc[ph][r + 1], sl2, nl4[(r + 1) >> 2][(r + 1) & 3]));
+      pk[ph][w] = pack2<T>(pf[ph][r], pf[ph][r + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Transposed operands of phases C (dO^T) and D (Q^T), slot m: (t2, db) =
+    // (m / 8, (m / 2) % 4) of each phase, shared by the two key halves.
+    V8 ta[2][2][NDB];
+    auto read_cd = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 32 && (m & 1) == 0) {
+        constexpr int ph = m >> 4, t2 = (m & 15) >> 3, db = (m >> 1) & 3;
+        ta[ph][t2][db] = trl.template tr<V8>(ph ? Qs : Ds_, db, t2);
+      }
+    };
+    static_for<kLA>([&](auto mc) { read_cd(mc); });
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value, t2 = m >> 3, db = (m >> 1) & 3, hf = m & 1;
+      const V8 pb = __builtin_bit_cast(V8, u32x4{pk[hf][4 * t2], pk[hf][4 * t2 + 1], pk[hf][4 * t2 + 2], pk[hf][4 * t2 + 3]});
+      if (hf) mfma_acc<T>(dv1[db], ta[0][t2][db], pb);
+      else mfma_acc<T>(dv0[db], ta[0][t2][db], pb);
+      read_cd(std::integral_constant<int, m + kLA>{});
+      // dS: two per slot.
+      constexpr int ph = m >> 3, w = m & 7, r = 2 * w;
+      const float g0 = pf[ph][r] * (dpc[ph][r] - d4[r >> 2][r & 3]);
+      const float g1 = pf[ph][r + 1] * (dpc[ph][r + 1] - d4[(r + 1) >> 2][(r + 1) & 3]);
+      sk[ph][w] = pack2<T>(g0, g1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value, t2 = m >> 3, db = (m >> 1) & 3, hf = m & 1;
+      const V8 sb = __builtin_bit_cast(V8, u32x4{sk[hf][4 * t2], sk[hf][4 * t2 + 1], sk[hf][4 * t2 + 2], sk[hf][4 * t2 + 3]});
+      if (hf) mfma_acc<T>(dk1[db], ta[1][t2][db], sb);
+      else mfma_acc<T>(dk0[db], ta[1][t2][db], sb);
+      read_cd(std::integral_constant<int, m + 16 + kLA>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  mfma_acc_drain(dk0, dk1, dv0, dv1);
+
+  const float vsc = a.dv_scale;
+  auto store_keys = [&](const f32x16 (&dk)[NDB], const f32x16 (&dv)[NDB], int my_key) {
+    if (my_key >= a.s_kv) return;
+    if (n_split == 1) {
+      uint16_t* dkp = (uint16_t*)a.dk + bi * a.dks.b + g * a.dks.h + (int64_t)my_key * a.dks.s;
+      uint16_t* dvp = (uint16_t*)a.dv + bi * a.dvs.b + g * a.dvs.h + (int64_t)my_key * a.dvs.s;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = db * 32 + 8 * rq + 4 * h;
+          u32x2 wk, wv;
+          wk.x = pack2<T>(dk[db][4 * rq] * a.dk_scale, dk[db][4 * rq + 1] * a.dk_scale);
+          wk.y = pack2<T>(dk[db][4 * rq + 2] * a.dk_scale, dk[db][4 * rq + 3] * a.dk_scale);
+          wv.x = pack2<T>(dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc);
+          wv.y = pack2<T>(dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc);
+          *(u32x2*)(dkp + d0) = wk;
+          *(u32x2*)(dvp + d0) = wv;
+        }
+    } else {
+      const int64_t plane = (int64_t)a.b * a.h_kv * a.s_kv * D;
+      const int64_t off = (int64_t)sp * plane + (((int64_t)bi * a.h_kv + g) * a.s_kv + my_key) * D;
+      float* pk = part + off;
+      float* pv = part + (int64_t)n_split * plane + off;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = db * 32 + 8 * rq + 4 * h;
+          *(f32x4*)(pk + d0) = f32x4{dk[db][4 * rq] * a.dk_scale, dk[db][4 * rq + 1] * a.dk_scale,
+                                     dk[db][4 * rq + 2] * a.dk_scale, dk[db][4 * rq + 3] * a.dk_scale};
+          *(f32x4*)(pv + d0) =
+              f32x4{dv[db][4 * rq] * vsc, dv[db][4 * rq + 1] * vsc, dv[db][4 * rq + 2] * vsc, dv[db][4 * rq + 3] * vsc};
+        }
+    }
+  };
+  store_keys(dk0, dv0, key0);
+  store_keys(dk1, dv1, key1);
+}
+
 // Sums the n_split fp32 partials of dK and dV in split order and rounds them.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int n_split, const float* part) {
@@ -697,7 +1000,12 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream, const TimingEvents& 
   float* part = n_split > 1 ? bwd_partials(a) : nullptr;
   const int n_kblk = (a.s_kv + kKvBlock - 1) / kKvBlock;
   const dim3 g1(n_kblk * a.b * a.h_kv * n_split);
-  if (a.causal)
+  if (D == 128 && MOD == kModNone) {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dkdv64_kernel<T, true>), g1, dim3(256), 0, stream, a, n_split, part);
+    else
+      hipLaunchKernelGGL((bwd_dkdv64_kernel<T, false>), g1, dim3(256), 0, stream, a, n_split, part);
+  } else if (a.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, MOD>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, MOD>), g1, dim3(512), 0, stream, a, n_kblk, n_split, part);
