@@ -135,7 +135,7 @@ def write_traffic_record(kernel: str, fetch_db: str, write_db: str, copy_fetch_d
     import json
     import sqlite3
 
-    short = {"bwd_dkdv": "bwd_dkdv_kernel<sdpa::Bf16T, 128, true, 0>",
+    short = {"bwd_dkdv": "bwd_dkdv64_kernel<sdpa::Bf16T, true>",
              "fwd": "fwd_mfma_kernel<sdpa::Bf16T, 128, true, 8, 0, 1>",
              "bwd_dq": "bwd_dq_kernel<sdpa::Bf16T, 128, true, 0>"}[kernel]
 
