@@ -445,11 +445,11 @@ template <typename T>
 __device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b);
 template <>
 __device__ __forceinline__ void mfma_acc<Bf16T>(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 template <>
 __device__ __forceinline__ void mfma_acc<F16T>(f32x16& c, f16x8 a, f16x8 b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // 24 wait states: more than an MFMA result needs before a VALU or
 // v_accvgpr_read reads it. The accumulators pass through empty statements
@@ -552,9 +552,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
   u32x4 qreg[QPT], dreg[QPT];
   float lreg = 0.f, creg = 0.f;
   bool lvalid = false;
-  auto load_tile = [&](int it) {
-    const int hq = hq_base + it / nq;
-    const int q0 = (qt0 + it % nq) * kQTile;
+  // Tile cursors: (query head, query tile) of the next load, query tile of
+  // the next computed tile (no divisions in the loop).
+  int l_hq = hq_base, l_qt = qt0, c_qt = qt0;
+  auto load_tile = [&]() {
+    const int hq = l_hq;
+    const int q0 = l_qt * kQTile;
+    if (++l_qt == n_qt) {
+      l_qt = qt0;
+      ++l_hq;
+    }
     const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h + (int64_t)q0 * a.qs.s;
     const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)q0 * a.dos.s;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2));
@@ -573,9 +580,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     }
   };
 
-  if (n_it > 0) load_tile(0);
+  if (n_it > 0) load_tile();
   for (int it = 0; it < n_it; ++it) {
-    const int q0 = (qt0 + it % nq) * kQTile;
+    const int q0 = c_qt * kQTile;
+    if (++c_qt == n_qt) c_qt = qt0;
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
       nlse2s[tid] = (lvalid && lreg != -INFINITY) ? -lreg * kLog2e : 0.f;
       dels[tid] = lvalid ? creg : 0.f;
     }
-    if (it + 1 < n_it) load_tile(it + 1);
+    if (it + 1 < n_it) load_tile();
     __syncthreads();  // this tile is in LDS
     // A tile whose queries all precede this wave's keys is computed anyway,
     // fully masked (it adds zeros): the SIMD has no other wave to give the
