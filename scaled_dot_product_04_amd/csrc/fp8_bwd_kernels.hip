@@ -343,19 +343,31 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
   int cur_qt = qt0 - 1;
   int b3 = 0;             // buffer of the tile being computed among the three-deep ones
   bool prev_live = false;  // the previous tile had work for this key slice (dK wave)
-  for (int it = 0; it < n_it; ++it) {
+  // Start of iteration `it`, the same in both roles (every wave meets the
+  // same barriers): advance the tile cursor, barrier, stage the next tile.
+  auto begin_tile = [&](int it, int& q0) {
     const int buf = it & 1;
-    const int b3n = b3 == 2 ? 0 : b3 + 1, b3p = b3 == 0 ? 2 : b3 - 1;
+    const int b3n = b3 == 2 ? 0 : b3 + 1;
     cur_qt = cur_qt + 1 == qt0 + nq ? qt0 : cur_qt + 1;
-    const int q0 = cur_qt * kT8;
+    q0 = cur_qt * kT8;
     __syncthreads();  // tile `it` and P of tile it - 1 are in LDS; nothing still reads the buffers written next
     if (it + 1 < n_it) {
       store_tile(buf ^ 1, b3n);
       if (it + 2 < n_it) load_tile();
     }
-    // A tile whose queries all precede this slice's keys has no work.
-    const bool live = !(CAUSAL && q0 + kT8 - 1 + L.off < kw0);
-    if (role_dk) {
+  };
+  // Each role runs its own loop, so that its accumulators are updated in one
+  // place: with both roles' updates in one loop body the compiler gave them
+  // two register ranges and copied the 64 accumulator registers from one to
+  // the other and back every tile.
+  if (role_dk) {
+    for (int it = 0; it < n_it; ++it) {
+      const int buf = it & 1;
+      const int b3n = b3 == 2 ? 0 : b3 + 1, b3p = b3 == 0 ? 2 : b3 - 1;
+      int q0;
+      begin_tile(it, q0);
+      // A tile whose queries all precede this slice's keys has no work.
+      const bool live = !(CAUSAL && q0 + kT8 - 1 + L.off < kw0);
       if (prev_live) dk_finish(buf ^ 1, b3p);
       if (live) {
 #pragma unroll
@@ -368,52 +380,59 @@ __global__ __launch_bounds__(kNT8, 1) void bwd8_dkdv_kernel(BwdArgs a, int n_spl
         }
       }
       prev_live = live;
-    } else if (live) {
-      const bool need_mask = (q0 + kT8 > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
-      // The body exists with and without the mask, each one branch-free: a
-      // mask branch inside it would split it into blocks across which the
-      // hoisted operand reads stay live.
-      auto dv_body = [&](auto masked) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked)::value;
-        uint32_t pk[8];
-        u32x4 ph[4];  // P * scale_p as fp16 pairs, for the dK wave
+      b3 = b3n;
+    }
+  } else {
+    for (int it = 0; it < n_it; ++it) {
+      const int buf = it & 1;
+      const int b3n = b3 == 2 ? 0 : b3 + 1;
+      int q0;
+      begin_tile(it, q0);
+      const bool live = !(CAUSAL && q0 + kT8 - 1 + L.off < kw0);
+      if (live) {
+        const bool need_mask = (q0 + kT8 > L.lq) || (kw0 + 32 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 31);
+        // The body exists with and without the mask, each one branch-free: a
+        // mask branch inside it would split it into blocks across which the
+        // hoisted operand reads stay live.
+        auto dv_body = [&](auto masked) __attribute__((always_inline)) -> i32x8 {
+          constexpr bool MASKED = decltype(masked)::value;
+          uint32_t pk[8];
+          u32x4 ph[4];  // P * scale_p as fp16 pairs, for the dK wave
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          // S for tile rows 32 nb + 16 h + r (register r) x this lane's key.
-          f32x16 s = f32x16{};
+          for (int nb = 0; nb < 2; ++nb) {
+            // S for tile rows 32 nb + 16 h + r (register r) x this lane's key.
+            f32x16 s = f32x16{};
 #pragma unroll
-          for (int t = 0; t < NKS; ++t)
-            s = mfma8<0, 0>(lds_op32(&Qr[b3][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], s);
-          if (MASKED) {
+            for (int t = 0; t < NKS; ++t)
+              s = mfma8<0, 0>(lds_op32(&Qr[b3][nb * 32 * G::RSTR + rowoff + 64 * t]), kvf[t], s);
+            if (MASKED) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qi = q0 + 32 * nb + 16 * h + r;
-              if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                const int qi = q0 + 32 * nb + 16 * h + r;
+                if (qi >= L.lq || my_key >= L.lk || (CAUSAL && my_key > qi + L.off)) s[r] = -INFINITY;
+              }
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const f32x4 l4 = *(const f32x4*)(&lse2s[buf][32 * nb + 16 * h + 4 * w]);
+              float p[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * w + e], sl2, -l4[e]));  // P * scale_p
+              pk[4 * nb + w] = pack4_fp8<false>(p[0], p[1], p[2], p[3]);
+              ph[2 * nb + w / 2][2 * (w % 2)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+              ph[2 * nb + w / 2][2 * (w % 2) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
             }
           }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f32x4 l4 = *(const f32x4*)(&lse2s[buf][32 * nb + 16 * h + 4 * w]);
-            float p[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * w + e], sl2, -l4[e]));  // P * scale_p
-            pk[4 * nb + w] = pack4_fp8<false>(p[0], p[1], p[2], p[3]);
-            ph[2 * nb + w / 2][2 * (w % 2)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
-            ph[2 * nb + w / 2][2 * (w % 2) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) *(u32x4*)(&Px[buf][pxoff + 16 * c]) = ph[c];
-        const i32x8 pb = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+          for (int c = 0; c < 4; ++c) *(u32x4*)(&Px[buf][pxoff + 16 * c]) = ph[c];
+          return i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+        };
+        const i32x8 pb = need_mask ? dv_body(std::true_type{}) : dv_body(std::false_type{});
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] = mfma8<FDO, 0>(lds_tr_op<D>(&Dr[buf][troff + 32 * db]), pb, acc[db]);
-      };
-      if (need_mask)
-        dv_body(std::true_type{});
-      else
-        dv_body(std::false_type{});
+      }
+      b3 = b3n;
     }
-    b3 = b3n;
   }
   // The last tile's dS: its P was written in the last step.
   __syncthreads();
