@@ -492,8 +492,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
   __shared__ __attribute__((aligned(16))) uint16_t QD[2 * kQTile * D];
   uint16_t* const Qs = QD;
   uint16_t* const Ds_ = QD + kQTile * D;
-  __shared__ __attribute__((aligned(16))) float nlse2s[kQTile];  // -LSE * log2 e
-  __shared__ __attribute__((aligned(16))) float dels[kQTile];
+  // -LSE log2 e and D of the current tile's rows, one copy per wave (lane l
+  // holds row l % 32): each wave writes and reads its own copy.
+  __shared__ __attribute__((aligned(16))) float nls[4][64];
+  __shared__ __attribute__((aligned(16))) float dls[4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
@@ -549,53 +551,84 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     doff[i] = (uint32_t)(sr * a.dos.s * 2 + scc * 16);
     sdst[i] = sr * D + ((scc ^ bswz<D>(sr)) * 8);
   }
+  // The tile walk: (query head, query tile) pairs, tiles qt0 .. n_qt - 1 of
+  // each head of the slice. The next tile to load is tracked by running
+  // addresses (Q and dO tile bytes, LSE / D row of its first query) that move
+  // one tile down the head, or from a head's last tile to the next head's
+  // tile qt0: no index arithmetic per tile.
+  const int64_t tq = (int64_t)kQTile * a.qs.s * 2, td = (int64_t)kQTile * a.dos.s * 2;
+  const int64_t wq = (int64_t)a.qs.h * 2 - (int64_t)(nq - 1) * tq;
+  const int64_t wd = (int64_t)a.dos.h * 2 - (int64_t)(nq - 1) * td;
+  const int64_t wr = (int64_t)a.s_q - (int64_t)(nq - 1) * kQTile;
+  const char* qn = (const char*)a.q + (bi * a.qs.b + hq_base * a.qs.h + (int64_t)qt0 * kQTile * a.qs.s) * 2;
+  const char* dn = (const char*)a.dout + (bi * a.dos.b + hq_base * a.dos.h + (int64_t)qt0 * kQTile * a.dos.s) * 2;
+  int64_t rn = ((int64_t)bi * a.h_q + hq_base) * a.s_q + qt0 * kQTile;
+  // Bytes a tile may read: all its rows, or up to row lq - 1 in a head's
+  // last tile (rows past it read as zero).
+  const uint32_t qfull = tile_bytes(0, kQTile, a.qs.s, D, 2), dfull = tile_bytes(0, kQTile, a.dos.s, D, 2);
+  const uint32_t qlast = tile_bytes((n_qt - 1) * kQTile, L.lq, a.qs.s, D, 2);
+  const uint32_t dlast = tile_bytes((n_qt - 1) * kQTile, L.lq, a.dos.s, D, 2);
   u32x4 qreg[QPT], dreg[QPT];
   float lreg = 0.f, creg = 0.f;
   bool lvalid = false;
-  // Tile cursors: (query head, query tile) of the next load, query tile of
-  // the next computed tile (no divisions in the loop).
-  int l_hq = hq_base, l_qt = qt0, c_qt = qt0;
-  auto load_tile = [&]() {
-    const int hq = l_hq;
-    const int q0 = l_qt * kQTile;
-    if (++l_qt == n_qt) {
-      l_qt = qt0;
-      ++l_hq;
-    }
-    const uint16_t* qp = (const uint16_t*)a.q + bi * a.qs.b + hq * a.qs.h + (int64_t)q0 * a.qs.s;
-    const uint16_t* dop = (const uint16_t*)a.dout + bi * a.dos.b + hq * a.dos.h + (int64_t)q0 * a.dos.s;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, tile_bytes(q0, L.lq, a.qs.s, D, 2));
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop, tile_bytes(q0, L.lq, a.dos.s, D, 2));
+  int l_qt = qt0, c_qt = qt0;  // query tile of the next load, of the next computed tile
+  // Loading a tile takes four steps, issued in separate MFMA slots: buffer
+  // descriptors (zero bytes past the last tile, so those loads return zeros
+  // and touch no memory), the Q / dO loads, the LSE / D loads of row
+  // min(lane % 32, last valid row), the cursor step.
+  __amdgpu_buffer_rsrc_t rq, rd, rl, rc;
+  int lq0 = 0;
+  auto tile_rsrc = [&](bool more) {
+    const bool last = l_qt == n_qt - 1;
+    lq0 = l_qt * kQTile;
+    rq = make_rsrc(qn, more ? (last ? qlast : qfull) : 0u);
+    rd = make_rsrc(dn, more ? (last ? dlast : dfull) : 0u);
+    rl = make_rsrc(a.lse + rn, more ? 4u * kQTile : 0u);
+    rc = make_rsrc(a.delta + rn, more ? 4u * kQTile : 0u);
+  };
+  auto tile_loads = [&]() {
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
-      qreg[i] = buf_load16(qr, qoff[i]);
-      dreg[i] = buf_load16(dr, doff[i]);
-    }
-    if (tid < kQTile) {
-      const int qi = q0 + tid;
-      lvalid = qi < L.lq;
-      const int64_t row = ((int64_t)bi * a.h_q + hq) * a.s_q + min(qi, L.lq - 1);
-      lreg = a.lse[row];
-      creg = a.delta[row];
+      qreg[i] = buf_load16(rq, qoff[i]);
+      dreg[i] = buf_load16(rd, doff[i]);
     }
   };
+  auto tile_stats = [&]() {
+    const int l = lane & 31;
+    lvalid = lq0 + l < L.lq;
+    const uint32_t o = (uint32_t)min(l, max(L.lq - 1 - lq0, 0)) * 4u;
+    lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, o, 0, 0));
+    creg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, o, 0, 0));
+  };
+  auto tile_next = [&]() {
+    const bool last = l_qt == n_qt - 1;
+    l_qt = last ? qt0 : l_qt + 1;
+    qn += last ? wq : tq;
+    dn += last ? wd : td;
+    rn += last ? wr : (int64_t)kQTile;
+  };
 
-  if (n_it > 0) load_tile();
+  if (n_it > 0) {
+    tile_rsrc(true);
+    tile_loads();
+    tile_stats();
+    tile_next();
+  }
   for (int it = 0; it < n_it; ++it) {
     const int q0 = c_qt * kQTile;
-    if (++c_qt == n_qt) c_qt = qt0;
+    c_qt = c_qt == n_qt - 1 ? qt0 : c_qt + 1;
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
       *(u32x4*)(&Qs[sdst[i]]) = qreg[i];
       *(u32x4*)(&Ds_[sdst[i]]) = dreg[i];
     }
-    if (tid < kQTile) {
-      nlse2s[tid] = (lvalid && lreg != -INFINITY) ? -lreg * kLog2e : 0.f;
-      dels[tid] = lvalid ? creg : 0.f;
-    }
-    if (it + 1 < n_it) load_tile();
+    // A row past lq, or one that sees no key, gets -LSE = -inf: its weights
+    // are exp2(-inf) = 0 whatever its (zero or masked) scores.
+    nls[wave][lane] = (lvalid && lreg != -INFINITY) ? -lreg * kLog2e : -INFINITY;
+    dls[wave][lane] = lvalid ? creg : 0.f;
     __syncthreads();  // this tile is in LDS
+    const bool more = it + 1 < n_it;
     // A tile whose queries all precede this wave's keys is computed anyway,
     // fully masked (it adds zeros): the SIMD has no other wave to give the
     // time to, and a branch around the accumulation makes the register
@@ -604,12 +637,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     // Four phases of 16 MFMA slots each; a scheduling fence closes every
     // slot, so the vector work placed in a slot issues beside that slot's
     // MFMA, and every LDS operand is read kLA slots before its MFMA:
-    //   A: S = Q K^T (both key halves share each Q read)
+    //   A: S = Q K^T (both key halves share each Q read), beside it the
+    //      next tile's loads
     //   B: dP = dO V^T, beside it P = exp2(S scale log2 e - LSE log2 e)
     //   C: dV^T += dO^T P (AGPR accumulators), beside it dS = P (dP - D)
     //   D: dK^T += Q^T dS
     constexpr int kLA = 4;
-    const bool need_mask = (q0 + kQTile > L.lq) || (kw0 + 64 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 63);
+    const bool need_mask = (kw0 + 64 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 63);
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dpc[2] = {f32x16{}, f32x16{}};
     V8 ra[8], rb[2][8];   // phase A / B row operands: Q or dO (shared), K or V per half
     f32x4 nl4[4], d4[4];  // -LSE log2 e and D of the lane's 16 query rows
@@ -628,23 +662,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     };
     static_for<kLA>([&](auto mc) { read_ab(mc); });
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) nl4[r4] = *(const f32x4*)(&nlse2s[8 * r4 + 4 * h]);
+    for (int r4 = 0; r4 < 4; ++r4) nl4[r4] = *(const f32x4*)(&nls[wave][8 * r4 + 4 * h]);
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
       sc[hf] = T::mfma(ra[t], rb[hf][t], sc[hf]);
       read_ab(std::integral_constant<int, m + kLA>{});
+      if constexpr (m == 1) tile_rsrc(more);
+      if constexpr (m == 2) tile_loads();
+      if constexpr (m == 3) tile_stats();
+      if constexpr (m == 4) tile_next();
       __builtin_amdgcn_sched_barrier(0);
     });
     if (need_mask) {
+      // Key k is hidden from row qi iff k > qi + off (causal) or k >= lk; with
+      // qi = q0 + 4 h + c, c = acc_row(r, 0), that is e > c for a per-half e.
+      const int qb = q0 + L.off + 4 * h;
+      const int e0 = key0 >= L.lk ? 0x7fffffff : CAUSAL ? key0 - qb : -0x7fffffff;
+      const int e1 = key1 >= L.lk ? 0x7fffffff : CAUSAL ? key1 - qb : -0x7fffffff;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + acc_row(r, h);
-        if (qi >= L.lq || key0 >= L.lk || (CAUSAL && key0 > qi + L.off)) sc[0][r] = -INFINITY;
-        if (qi >= L.lq || key1 >= L.lk || (CAUSAL && key1 > qi + L.off)) sc[1][r] = -INFINITY;
+        if (e0 > acc_row(r, 0)) sc[0][r] = -INFINITY;
+        if (e1 > acc_row(r, 0)) sc[1][r] = -INFINITY;
       }
     }
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) d4[r4] = *(const f32x4*)(&dels[8 * r4 + 4 * h]);
+    for (int r4 = 0; r4 < 4; ++r4) d4[r4] = *(const f32x4*)(&dls[wave][8 * r4 + 4 * h]);
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
       dpc[hf] = T::mfma(ra[t], rb[hf][t], dpc[hf]);
