@@ -106,7 +106,7 @@ struct TrLaneB {
 
 // A tile of R rows x D 16-bit elements in flight as 16-byte row chunks
 // (NT threads), written to LDS row-major in the bswz layout. Buffer loads;
-// rows past the end of the tensor read as zero.
+// rows past the descriptor's bytes read as zero.
 template <int R, int D, int NT>
 struct BswzTile {
   static constexpr int CH = D / 8;
@@ -127,8 +127,10 @@ struct BswzTile {
       dst[i] = r * D + ((cc ^ bswz<D>(r)) * 8);
     }
   }
-  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_rows) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, tile_bytes(row0, n_rows, stride, D, 2));
+  // Loads rows row0.. with a descriptor that allows `bytes` bytes from row0
+  // (tile_bytes; 0: every load returns zeros and reads no memory).
+  __device__ __forceinline__ void load(const uint16_t* base, int row0, uint32_t bytes) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * stride, bytes);
 #pragma unroll
     for (int i = 0; i < NC; ++i) v[i] = buf_load16(rs, off[i]);
   }
@@ -889,9 +891,16 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
   KvTile kreg, vreg;
   kreg.init(a.ks.s, tid);
   vreg.init(a.vs.s, tid);
-  auto load_tile = [&](int k0) {
-    kreg.load(kp, k0, L.lk);  // keys at or past lk read as zero
-    vreg.load(vp, k0, L.lk);
+  // Bytes a tile may read: all its rows, or up to key lk - 1 in the last
+  // tile (keys at or past lk read as zero); none past the last tile, so the
+  // loads issued there read nothing and need no branch.
+  const uint32_t kfull = tile_bytes(0, kKTile, a.ks.s, D, 2), vfull = tile_bytes(0, kKTile, a.vs.s, D, 2);
+  const uint32_t klast = tile_bytes((n_tiles - 1) * kKTile, L.lk, a.ks.s, D, 2);
+  const uint32_t vlast = tile_bytes((n_tiles - 1) * kKTile, L.lk, a.vs.s, D, 2);
+  auto load_tile = [&](int tile) {
+    const bool last = tile == n_tiles - 1, none = tile >= n_tiles;
+    kreg.load(kp, tile * kKTile, none ? 0u : last ? klast : kfull);
+    vreg.load(vp, tile * kKTile, none ? 0u : last ? vlast : vfull);
   };
   auto store_tile = [&](int buf) {
     kreg.store(Ks[buf]);
@@ -900,18 +909,17 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
-    if (n_tiles > 1) load_tile(kKTile);
+    load_tile(1);
   }
   // One K/V tile. Unrolled by two, `buf` is a constant at each call, so every
   // LDS operand address is a per-lane offset plus an immediate instead of an
-  // offset combined with a run-time buffer base.
+  // offset combined with a run-time buffer base. The other buffer is written
+  // every step (past the last tile with zeros nobody reads).
   auto step = [&](const int tile, const int buf) {
     const int k0 = tile * kKTile;
     __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
-    if (tile + 1 < n_tiles) {
-      store_tile(buf ^ 1);
-      if (tile + 2 < n_tiles) load_tile((tile + 2) * kKTile);
-    }
+    store_tile(buf ^ 1);
+    load_tile(tile + 2);
     if (CAUSAL && k0 > q0 + 31 + L.off) return;  // every key of the tile is above this wave's rows
     f32x16 s[NSB], dp[NSB];
 #pragma unroll
@@ -939,13 +947,14 @@ __global__ __launch_bounds__(64 * dq_waves(D), 8 / dq_waves(D)) void bwd_dq_kern
     }
     const bool need_mask = (k0 + kKTile > L.lk) || (CAUSAL && k0 + kKTile - 1 > q0 + L.off);
     if (need_mask) {
+      // Key k0 + c (c = 32 nb + acc_row(r, h)) is hidden from this row iff it
+      // is past the row's last visible key: one compare against a constant.
+      const int lim = (CAUSAL ? min(L.lk - 1, my_q + L.off) : L.lk - 1) - k0 - 4 * h;
 #pragma unroll
       for (int nb = 0; nb < NSB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + nb * 32 + acc_row(r, h);
-          if (key >= L.lk || (CAUSAL && key > my_q + L.off)) s[nb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + acc_row(r, 0) > lim) s[nb][r] = -INFINITY;
     }
     // Score modifiers of this query row and the tile's keys, log2 units.
     float madd[NSB][16];
