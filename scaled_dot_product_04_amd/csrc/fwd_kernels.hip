@@ -160,10 +160,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
   SwzLaneF<D> sl;
   sl.init(lane);
   u32x4 kreg[KCH];
-  auto load_tile = [&](int k0) {
-    // Rows at or past lk read as zero (never the caller's padding).
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
+  // Bytes a tile's descriptor allows: every row of a full tile, rows up to
+  // lk - 1 in the last one (rows at or past lk read as zero, never the
+  // caller's padding), none past the last tile (its loads read nothing).
+  const uint32_t kfull = tile_bytes(0, kBN, a.ks.s, D, 2), vfull = tile_bytes(0, kBN, a.vs.s, D, 2);
+  const uint32_t klast = tile_bytes((n_tiles - 1) * kBN, L.lk, a.ks.s, D, 2);
+  const uint32_t vlast = tile_bytes((n_tiles - 1) * kBN, L.lk, a.vs.s, D, 2);
+  auto load_tile = [&](int tile) {
+    const int k0 = tile * kBN;
+    const bool last = tile == n_tiles - 1, none = tile >= n_tiles;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, none ? 0u : last ? klast : kfull);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, none ? 0u : last ? vlast : vfull);
     uint32_t ko = koff0, vo = voff0;
     asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
@@ -187,81 +194,93 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a, in
     if (n_tiles > 0) {
       load_tile(0);
       store_tile(0);
-      if (n_tiles > 1) load_tile(kBN);
+      load_tile(1);
     }
 
     for (int tile = 0; tile < n_tiles; ++tile) {
       const int k0 = tile * kBN;
       const int buf = tile & 1;
       __syncthreads();  // buffer `buf` is complete; buffer buf^1 is no longer read
-      if (tile + 1 < n_tiles) {
+      // Staging of tile + 1 (registers -> the other buffer) and the loads of
+      // tile + 2: every thread takes part, every step (past the last tile the
+      // stores write zeros nobody reads). A wave that computes the tile
+      // stages after its score products, beside the exponentials, so the
+      // scores start right after the barrier.
+      auto stage = [&]() {
         store_tile(buf ^ 1);
-        if (tile + 2 < n_tiles) load_tile((tile + 2) * kBN);
-      }
+        load_tile(tile + 2);
+      };
       const int kg0 = k0 + kg;  // first key of this wave's part of the tile
-      if (CAUSAL && kg0 > q0 + 31 + L.off) continue;  // every key of it is above this wave's rows
+      // Every key of it above this wave's rows: the wave only stages. (One
+      // staging call site: with a second one in the skip branch the register
+      // allocator kept two copies of the staging registers and spilled.)
+      const bool skip = CAUSAL && kg0 > q0 + 31 + L.off;
 
       // S^T = K Q^T for this wave's GBN keys of the tile.
       f32x16 sacc[NSB];
+      if (!skip) {
 #pragma unroll
-      for (int nb = 0; nb < NSB; ++nb) {
-        sacc[nb] = f32x16{};
+        for (int nb = 0; nb < NSB; ++nb) {
+          sacc[nb] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < NKS; ++t) {
-          const V8 kf = *(const V8*)(&Ks[buf][(kg + nb * 32 + j) * KSTR + 16 * t + 8 * h]);
-          sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
-        }
-      }
-      if constexpr (MOD == kModNone) {
-        // Schedule: the K operand reads run kLook MFMAs ahead (the default
-        // schedule read each operand just before its MFMA). 1.5 % on the hd128
-        // forward, no extra spills.
-        __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // LDS reads
-#pragma unroll
-        for (int i = 0; i < NSB * NKS - kLook; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
-      }
-      if (MOD == kModNone && fast && tile == 0) {
-        // Starting max: this row's score against the wave's first key kg
-        // (unmasked; key 0 without a key split). A row's visible keys are a
-        // prefix, so a row that sees any key this wave takes sees that one,
-        // and an actual score is a lower bound of the row max: no weight
-        // underflows for want of a larger one. (Rows that see none of the
-        // wave's keys get no weight at all.) A row whose max is key 0, like
-        // causal row 0, gets the weight exp2(0) = 1 for it, as with an exact
-        // max. The first key is accumulator register 0 of the lower half-wave.
-        m_run = halves_swap(sacc[0][0]).x * sc;  // lane j's value in both halves
-      }
-      if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
-#pragma unroll
-        for (int nb = 0; nb < NSB; ++nb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int key0 = kg0 + nb * 32 + 8 * q4 + 4 * h;
-            const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
-              sacc[nb][4 * q4 + e] = fmaf(sacc[nb][4 * q4 + e], sl2, fmaf(bv[e], kLog2e, -slope2 * dist));
-            }
+          for (int t = 0; t < NKS; ++t) {
+            const V8 kf = *(const V8*)(&Ks[buf][(kg + nb * 32 + j) * KSTR + 16 * t + 8 * h]);
+            sacc[nb] = T::mfma(kf, qf[t], sacc[nb]);
           }
-      }
-      // Causal / key-length mask (only tiles that cross the diagonal or lk).
-      const bool need_mask = (kg0 + GBN > L.lk) || (CAUSAL && kg0 + GBN - 1 > q0 + L.off);
-      if (need_mask) {
-        // Key k0 + c (c = nb * 32 + acc_row(r, h)) is visible iff k0 + c <= last,
-        // the last key this row sees; one compare against a constant per score.
-        const int last = CAUSAL ? min(L.lk - 1, my_q + L.off) : L.lk - 1;
-        const int lim = last - kg0 - 4 * h;
+        }
+        if constexpr (MOD == kModNone) {
+          // Schedule: the K operand reads run kLook MFMAs ahead (the default
+          // schedule read each operand just before its MFMA). 1.5 % on the hd128
+          // forward, no extra spills.
+          __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // LDS reads
 #pragma unroll
-        for (int nb = 0; nb < NSB; ++nb)
+          for (int i = 0; i < NSB * NKS - kLook; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
+        }
+        if (MOD == kModNone && fast && tile == 0) {
+          // Starting max: this row's score against the wave's first key kg
+          // (unmasked; key 0 without a key split). A row's visible keys are a
+          // prefix, so a row that sees any key this wave takes sees that one,
+          // and an actual score is a lower bound of the row max: no weight
+          // underflows for want of a larger one. (Rows that see none of the
+          // wave's keys get no weight at all.) A row whose max is key 0, like
+          // causal row 0, gets the weight exp2(0) = 1 for it, as with an exact
+          // max. The first key is accumulator register 0 of the lower half-wave.
+          m_run = halves_swap(sacc[0][0]).x * sc;  // lane j's value in both halves
+        }
+        if (MOD) {  // S * scale * log2e + (bias - slope * |i + off - j|) * log2e
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (nb * 32 + acc_row(r, 0) > lim) sacc[nb][r] = -INFINITY;
+          for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int key0 = kg0 + nb * 32 + 8 * q4 + 4 * h;
+              const f32x4 bv = MOD == kModAll ? bias4<T>(bias_row, a.mod.bias_f32, key0, a.s_kv) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float dist = fabsf((float)(my_q + L.off - (key0 + e)));
+                sacc[nb][4 * q4 + e] = fmaf(sacc[nb][4 * q4 + e], sl2, fmaf(bv[e], kLog2e, -slope2 * dist));
+              }
+            }
+        }
+        // Causal / key-length mask (only tiles that cross the diagonal or lk).
+        const bool need_mask = (kg0 + GBN > L.lk) || (CAUSAL && kg0 + GBN - 1 > q0 + L.off);
+        if (need_mask) {
+          // Key k0 + c (c = nb * 32 + acc_row(r, h)) is visible iff k0 + c <= last,
+          // the last key this row sees; one compare against a constant per score.
+          const int last = CAUSAL ? min(L.lk - 1, my_q + L.off) : L.lk - 1;
+          const int lim = last - kg0 - 4 * h;
+#pragma unroll
+          for (int nb = 0; nb < NSB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (nb * 32 + acc_row(r, 0) > lim) sacc[nb][r] = -INFINITY;
+        }
       }
+      stage();
+      if (skip) continue;
       uint32_t pk[NSB][8];
       float lsum0 = 0.f, lsum1 = 0.f;
       if (MOD == kModNone && fast) {
