@@ -439,19 +439,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 // MFMA with its accumulator in AGPRs. The kernels of this file are compiled
 // with VGPR accumulators; this form keeps a long-lived accumulator out of the
 // 256 architectural VGPRs at one wave per SIMD (512 registers), and leaves
-// the VGPRs to the VALU work that runs beside the matrix core. The two wait
-// states cover a VALU write of an operand just before (the compiler does not
-// track hazards into inline assembly); readers of the accumulators must wait
-// for the last MFMA (mfma_acc_drain).
+// the VGPRs to the VALU work that runs beside the matrix core. The compiler
+// does not track hazards into inline assembly: an operand written by a VALU
+// instruction needs two wait states before the MFMA reads it. The operands
+// here are LDS reads and values packed a phase earlier, and a test compiles
+// this file to assembly and checks that no VALU write of an operand lands in
+// the two instructions before one of these MFMAs. Readers of the
+// accumulators must wait for the last MFMA (mfma_acc_drain).
 template <typename T>
 __device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b);
 template <>
 __device__ __forceinline__ void mfma_acc<Bf16T>(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 template <>
 __device__ __forceinline__ void mfma_acc<F16T>(f32x16& c, f16x8 a, f16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // 24 wait states: more than an MFMA result needs before a VALU or
 // v_accvgpr_read reads it. The accumulators pass through empty statements
@@ -475,9 +478,12 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16 (&a0)[N], f32x16 (&a1)[N],
 // Q^T, dO^T transposed operand read from LDS feeds two MFMAs, one per half,
 // and the dK^T / dV^T accumulators (256 registers) live in AGPRs, where the
 // vector work of the same wave can issue beside the MFMAs that update them.
-// With one wave per SIMD nothing hides a pause, so the tile body is a fixed
-// slot schedule (four phases of 16 MFMAs, operands read four slots ahead).
-// Same-box A/B at b2 h16 s8192 d128 causal: backward 1.849 -> 1.784 ms.
+// The wave's K rows stay in registers for the whole kernel (64 VGPRs, the B
+// operands of S = Q K^T); only the V rows sit in LDS, which leaves room for
+// two Q/dO tile buffers: the next tile is staged into the other buffer while
+// the current one is computed, one barrier per tile. With one wave per SIMD
+// nothing hides a pause, so the tile body is a fixed slot schedule (four
+// phases of 16 MFMAs, operands read four slots ahead).
 template <typename T, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_split, float* part) {
   typedef typename T::vec8 V8;
@@ -487,17 +493,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
   constexpr int KVC = kKvBlock * CH / NT;
   constexpr int QCH = kQTile * CH;
   constexpr int QPT = QCH / NT;
+  constexpr int TB = 2 * kQTile * D;  // one tile buffer: Q rows, then dO rows
   static_assert(KVC * NT == kKvBlock * CH && QPT * NT == QCH, "tile / thread mismatch");
-  // K/V block as in bwd_dkdv_kernel: row r = K row r, V row r, 16 bytes of padding.
-  constexpr int KVP = 2 * D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t KV[kKvBlock * KVP];
-  __shared__ __attribute__((aligned(16))) uint16_t QD[2 * kQTile * D];
-  uint16_t* const Qs = QD;
-  uint16_t* const Ds_ = QD + kQTile * D;
-  // -LSE log2 e and D of the current tile's rows, one copy per wave (lane l
-  // holds row l % 32): each wave writes and reads its own copy.
-  __shared__ __attribute__((aligned(16))) float nls[4][64];
-  __shared__ __attribute__((aligned(16))) float dls[4][64];
+  // V rows padded by 16 bytes: the 16 rows a lane group reads start 4 banks apart.
+  constexpr int VP = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kKvBlock * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t QD[2 * TB];
+  // -LSE log2 e and D of a tile's rows, per buffer and per wave (lane l holds
+  // row l % 32): each wave writes and reads its own copy.
+  __shared__ __attribute__((aligned(16))) float nls[2][4][64];
+  __shared__ __attribute__((aligned(16))) float dls[2][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j = lane & 31, h = lane >> 5;
@@ -514,17 +519,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
   const int key0 = kw0 + j, key1 = key0 + 32;
   const uint16_t* kp = (const uint16_t*)a.k + bi * a.ks.b + g * a.ks.h;
   const uint16_t* vp = (const uint16_t*)a.v + bi * a.vs.b + g * a.vs.h;
+  // The wave's K rows (key kw0 + 32 hf + j, elements 16 t + 8 h .. + 7 in
+  // lane (j, h)) straight into registers; the block's V rows into LDS. Keys
+  // at or past lk read as zero.
+  V8 kf[2][NKS];
   {
     const int k0 = kb * kKvBlock;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + (int64_t)k0 * a.ks.s, tile_bytes(k0, L.lk, a.ks.s, D, 2));
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + (int64_t)k0 * a.vs.s, tile_bytes(k0, L.lk, a.vs.s, D, 2));
 #pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int t = 0; t < NKS; ++t)
+        kf[hf][t] = __builtin_bit_cast(
+            V8, buf_load16(kr, (uint32_t)((wave * 64 + 32 * hf + j) * a.ks.s * 2 + (16 * t + 8 * h) * 2)));
+#pragma unroll
     for (int i = 0; i < KVC; ++i) {
       const int c = tid + NT * i;
       const int r = c / CH, cc = c % CH;
-      const int dst = r * KVP + cc * 8;
-      *(u32x4*)(&KV[dst]) = buf_load16(kr, (uint32_t)(r * a.ks.s * 2 + cc * 16));
-      *(u32x4*)(&KV[dst + D]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
+      *(u32x4*)(&Vs[r * VP + cc * 8]) = buf_load16(vr, (uint32_t)(r * a.vs.s * 2 + cc * 16));
     }
   }
   f32x16 dk0[NDB], dk1[NDB], dv0[NDB], dv1[NDB];
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
   int rowoff_q[NKS];
 #pragma unroll
   for (int t = 0; t < NKS; ++t) rowoff_q[t] = j * D + (((2 * t + h) ^ bswz<D>(j)) * 8);
-  const int kvoff = (wave * 64 + j) * KVP + 8 * h;  // half 1: + 32 rows, an immediate
+  const int voff = (wave * 64 + j) * VP + 8 * h;  // half 1: + 32 rows, an immediate
   TrLaneB<D> trl;
   trl.init(lane);
 
@@ -595,9 +608,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
       dreg[i] = buf_load16(rd, doff[i]);
     }
   };
-  auto tile_stats = [&]() {
+  auto tile_stats = [&](bool more) {
     const int l = lane & 31;
-    lvalid = lq0 + l < L.lq;
+    lvalid = more && lq0 + l < L.lq;
     const uint32_t o = (uint32_t)min(l, max(L.lq - 1 - lq0, 0)) * 4u;
     lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, o, 0, 0));
     creg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, o, 0, 0));
@@ -610,27 +623,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     rn += last ? wr : (int64_t)kQTile;
   };
 
-  if (n_it > 0) {
-    tile_rsrc(true);
-    tile_loads();
-    tile_stats();
-    tile_next();
-  }
-  for (int it = 0; it < n_it; ++it) {
-    const int q0 = c_qt * kQTile;
-    c_qt = c_qt == n_qt - 1 ? qt0 : c_qt + 1;
-    __syncthreads();  // every wave is done with the previous tile
+  // Registers (the next tile) -> tile buffer b. A row past lq, or one that
+  // sees no key, gets -LSE = -inf: its weights are exp2(-inf) = 0 whatever its
+  // (zero or masked) scores.
+  auto stage_regs = [&](int b) {
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
-      *(u32x4*)(&Qs[sdst[i]]) = qreg[i];
-      *(u32x4*)(&Ds_[sdst[i]]) = dreg[i];
+      *(u32x4*)(&QD[b * TB + sdst[i]]) = qreg[i];
+      *(u32x4*)(&QD[b * TB + kQTile * D + sdst[i]]) = dreg[i];
     }
-    // A row past lq, or one that sees no key, gets -LSE = -inf: its weights
-    // are exp2(-inf) = 0 whatever its (zero or masked) scores.
-    nls[wave][lane] = (lvalid && lreg != -INFINITY) ? -lreg * kLog2e : -INFINITY;
-    dls[wave][lane] = lvalid ? creg : 0.f;
-    __syncthreads();  // this tile is in LDS
-    const bool more = it + 1 < n_it;
+    // (Selects, not && : a short-circuit becomes a branch that would split
+    // the slot schedule this runs in.)
+    const bool ok = lvalid & (lreg != -INFINITY);
+    nls[b][wave][lane] = ok ? -lreg * kLog2e : -INFINITY;
+    dls[b][wave][lane] = lvalid ? creg : 0.f;
+  };
+  // The loop is unrolled by the two buffers (their LDS addresses become
+  // immediates) and runs an even number of tiles: a last padding tile has
+  // zero-byte loads, so it adds nothing (Q = dO = 0, -LSE = -inf).
+  const int n_it2 = (n_it + 1) & ~1;
+  if (n_it2 > 0) {
+    tile_rsrc(true);
+    tile_loads();
+    tile_stats(true);
+    tile_next();
+    stage_regs(0);
+    tile_rsrc(n_it > 1);
+    tile_loads();
+    tile_stats(n_it > 1);
+    tile_next();
+  }
+  auto step = [&](const int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const uint16_t* const Qs = QD + buf * TB;
+    const uint16_t* const Ds_ = Qs + kQTile * D;
+    const int q0 = c_qt * kQTile;
+    c_qt = c_qt == n_qt - 1 ? qt0 : c_qt + 1;
+    // Buffer `buf` holds tile it; every wave is done with tile it - 1, whose
+    // buffer takes tile it + 1 in phase D.
+    __syncthreads();
+    const bool more = it + 2 < n_it;
     // A tile whose queries all precede this wave's keys is computed anyway,
     // fully masked (it adds zeros): the SIMD has no other wave to give the
     // time to, and a branch around the accumulation makes the register
@@ -639,15 +671,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
     // Four phases of 16 MFMA slots each; a scheduling fence closes every
     // slot, so the vector work placed in a slot issues beside that slot's
     // MFMA, and every LDS operand is read kLA slots before its MFMA:
-    //   A: S = Q K^T (both key halves share each Q read), beside it the
-    //      next tile's loads
+    //   A: S = Q K^T (K from registers; both key halves share each Q read)
     //   B: dP = dO V^T, beside it P = exp2(S scale log2 e - LSE log2 e)
     //   C: dV^T += dO^T P (AGPR accumulators), beside it dS = P (dP - D)
-    //   D: dK^T += Q^T dS
+    //   D: dK^T += Q^T dS, beside it the staging of tile it + 1 (loaded a
+    //      step earlier) and the loads of tile it + 2
     constexpr int kLA = 4;
     const bool need_mask = (kw0 + 64 > L.lk) || (CAUSAL && q0 + L.off < kw0 + 63);
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dpc[2] = {f32x16{}, f32x16{}};
-    V8 ra[8], rb[2][8];   // phase A / B row operands: Q or dO (shared), K or V per half
+    V8 ra[8], rb[2][8];   // phase A / B row operands: Q or dO (shared), V per half
     f32x4 nl4[4], d4[4];  // -LSE log2 e and D of the lane's 16 query rows
     float pf[2][16];
     uint32_t pk[2][8], sk[2][8];
@@ -657,22 +689,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
       if constexpr (m < 32) {
         constexpr int t = (m & 15) >> 1, hf = m & 1;
         const uint16_t* tile = m < 16 ? Qs : Ds_;
-        const int kv = kvoff + (m < 16 ? 0 : D) + (hf ? 32 * KVP : 0) + 16 * t;
         if constexpr (hf == 0) ra[t] = *(const V8*)(&tile[rowoff_q[t]]);
-        rb[hf][t] = *(const V8*)(&KV[kv]);
+        if constexpr (m >= 16) rb[hf][t] = *(const V8*)(&Vs[voff + (hf ? 32 * VP : 0) + 16 * t]);
       }
     };
     static_for<kLA>([&](auto mc) { read_ab(mc); });
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) nl4[r4] = *(const f32x4*)(&nls[wave][8 * r4 + 4 * h]);
+    for (int r4 = 0; r4 < 4; ++r4) nl4[r4] = *(const f32x4*)(&nls[buf][wave][8 * r4 + 4 * h]);
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
-      sc[hf] = T::mfma(ra[t], rb[hf][t], sc[hf]);
+      sc[hf] = T::mfma(ra[t], kf[hf][t], sc[hf]);
       read_ab(std::integral_constant<int, m + kLA>{});
-      if constexpr (m == 1) tile_rsrc(more);
-      if constexpr (m == 2) tile_loads();
-      if constexpr (m == 3) tile_stats();
-      if constexpr (m == 4) tile_next();
       __builtin_amdgcn_sched_barrier(0);
     });
     if (need_mask) {
@@ -688,7 +715,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
       }
     }
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) d4[r4] = *(const f32x4*)(&dls[wave][8 * r4 + 4 * h]);
+    for (int r4 = 0; r4 < 4; ++r4) d4[r4] = *(const f32x4*)(&dls[buf][wave][8 * r4 + 4 * h]);
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value, t = m >> 1, hf = m & 1;
       dpc[hf] = T::mfma(ra[t], rb[hf][t], dpc[hf]);
@@ -730,8 +757,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv64_kernel(BwdArgs a, int n_spl
       if (hf) mfma_acc<T>(dk1[db], ta[1][t2][db], sb);
       else mfma_acc<T>(dk0[db], ta[1][t2][db], sb);
       read_cd(std::integral_constant<int, m + 16 + kLA>{});
+      if constexpr (m == 8) stage_regs(buf ^ 1);
+      if constexpr (m == 9) tile_rsrc(more);
+      if constexpr (m == 10) tile_loads();
+      if constexpr (m == 11) tile_stats(more);
+      if constexpr (m == 12) tile_next();
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+  for (int it = 0; it < n_it2; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    step(it + 1, std::integral_constant<int, 1>{});
   }
   mfma_acc_drain(dk0, dk1, dv0, dv1);
 
