@@ -425,53 +425,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kblk,
   }
 }
 
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (unrolled at
-// compile time, so array indices derived from i stay in registers).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// MFMA with its accumulator in AGPRs. The kernels of this file are compiled
-// with VGPR accumulators; this form keeps a long-lived accumulator out of the
-// 256 architectural VGPRs at one wave per SIMD (512 registers), and leaves
-// the VGPRs to the VALU work that runs beside the matrix core. The compiler
-// does not track hazards into inline assembly: an operand written by a VALU
-// instruction needs two wait states before the MFMA reads it. The operands
-// here are LDS reads and values packed a phase earlier, and a test compiles
-// this file to assembly and checks that no VALU write of an operand lands in
-// the two instructions before one of these MFMAs. Readers of the
-// accumulators must wait for the last MFMA (mfma_acc_drain).
-template <typename T>
-__device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b);
-template <>
-__device__ __forceinline__ void mfma_acc<Bf16T>(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-template <>
-__device__ __forceinline__ void mfma_acc<F16T>(f32x16& c, f16x8 a, f16x8 b) {
-  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-// 24 wait states: more than an MFMA result needs before a VALU or
-// v_accvgpr_read reads it. The accumulators pass through empty statements
-// ordered after the wait, so that no read of them moves above it (without
-// them the compiler hoisted the epilogue's AGPR reads over the wait).
-template <int N>
-__device__ __forceinline__ void mfma_acc_drain(f32x16 (&a0)[N], f32x16 (&a1)[N], f32x16 (&a2)[N], f32x16 (&a3)[N]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    asm volatile("" : "+a"(a0[i]));
-    asm volatile("" : "+a"(a1[i]));
-    asm volatile("" : "+a"(a2[i]));
-    asm volatile("" : "+a"(a3[i]));
-  }
-}
-
 // KV-stationary dK/dV at d = 128 without score modifiers, one wave per SIMD.
 // A workgroup has 4 waves and the same 256-key block as bwd_dkdv_kernel, but
 // wave w owns 64 keys (two 32-key halves): every Q, dO row operand and every

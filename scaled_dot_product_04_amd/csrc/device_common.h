@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace sdpa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -58,6 +60,52 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   typedef typename T::elem E;
   typedef E E2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), E2));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (unrolled at
+// compile time, so array indices derived from i stay in registers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// MFMA with its accumulator in AGPRs. The kernels are compiled with VGPR
+// accumulators; this form keeps a long-lived accumulator out of the
+// architectural VGPRs, and an MFMA whose accumulator is in AGPRs lets the
+// vector work of the same wave issue beside it. The compiler does not track
+// hazards into inline assembly: an operand written by a VALU instruction
+// needs two wait states before the MFMA reads it. The callers feed LDS reads
+// and values packed well before, and a test compiles the kernels to assembly
+// and checks that no VALU write of an operand lands in the two instructions
+// before one of these MFMAs. Readers of the accumulators must wait for the
+// last MFMA (mfma_acc_drain).
+template <typename T>
+__device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b);
+template <>
+__device__ __forceinline__ void mfma_acc<Bf16T>(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <>
+__device__ __forceinline__ void mfma_acc<F16T>(f32x16& c, f16x8 a, f16x8 b) {
+  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 24 wait states: more than an MFMA result needs before a VALU or
+// v_accvgpr_read reads it. The accumulators pass through empty statements
+// ordered after the wait, so that no read of them moves above it (without
+// them the compiler hoisted the epilogue's AGPR reads over the wait).
+template <int N, typename... A>
+__device__ __forceinline__ void mfma_acc_drain(f32x16 (&a0)[N], A&... rest) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  auto pin = [](f32x16 (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+a"(a[i]));
+  };
+  pin(a0);
+  (pin(rest), ...);
 }
 
 // Buffer resource for raw buffer loads of gfx9-class GPUs: `bytes` is the
