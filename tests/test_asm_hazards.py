@@ -13,7 +13,7 @@ import pytest
 
 from scaled_dot_product_04_amd import _build
 
-SRC = os.path.join(os.path.dirname(_build.__file__), "csrc", "bwd_kernels.hip")
+CSRC = os.path.join(os.path.dirname(_build.__file__), "csrc")
 
 
 def _regs(tok: str) -> set:
@@ -54,14 +54,14 @@ def test_scanner_flags_a_planted_hazard():
 
 
 @pytest.mark.skipif(shutil.which(_build.HIPCC) is None and not os.path.exists(_build.HIPCC), reason="hipcc not found")
-def test_dkdv64_asm_mfma_operands_have_wait_states(tmp_path):
-    out = tmp_path / "bwd.s"
-    cmd = [_build.HIPCC, *_build.FLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+@pytest.mark.parametrize("src,kernel", [("bwd_kernels.hip", "bwd_dkdv64_kernel")])
+def test_asm_mfma_operands_have_wait_states(tmp_path, src, kernel):
+    out = tmp_path / "k.s"
+    cmd = [_build.HIPCC, *_build.FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
-    for name in ["bwd_dkdv64_kernelINS_5Bf16TELb1E", "bwd_dkdv64_kernelINS_5Bf16TELb0E",
-                 "bwd_dkdv64_kernelINS_4F16TELb1E", "bwd_dkdv64_kernelINS_4F16TELb0E"]:
+    for name in [kernel + "INS_5Bf16TELb1E", kernel + "INS_5Bf16TELb0E", kernel + "INS_4F16TELb1E", kernel + "INS_4F16TELb0E"]:
         n, bad = find_hazards(_kernel_lines(asm, name))
         assert n > 0, name
         assert not bad, (name, bad[:3])
