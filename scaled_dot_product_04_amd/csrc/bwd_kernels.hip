@@ -26,8 +26,9 @@
 //     When a GQA/MQA group would leave the GPU underfilled, the group's query
 //     heads are split over several workgroups that write fp32 partials.
 //     At d = 128 without score modifiers the same block runs as 4 waves of
-//     64 keys (bwd_dkdv64_kernel): one wave per SIMD, AGPR accumulators, and
-//     each LDS operand read feeding two MFMAs.
+//     64 keys (bwd_dkdv64_kernel): one wave per SIMD, AGPR accumulators,
+//     each LDS operand read feeding two MFMAs, the wave's K rows in
+//     registers and two query-tile buffers (one barrier per tile).
 //  3. reduce: sums the partials of the splits in a fixed order.
 #include "device_common.h"
 #include "sdpa_internal.h"
